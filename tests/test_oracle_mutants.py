@@ -1,0 +1,54 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies ``oracle/q4_oracle.c``, changes one expression to a
+plausible bug (swapped nibbles, wrong offset, wrong scale index, a dropped
+term, a flipped sign, the wrong input row, a wrong exponent bias, a wrong
+pack shift), compiles the copy on the CPU and checks that at least one pin
+fails for it.  The real oracle passing every pin is ``test_oracle.py``.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "q4_oracle.c")
+
+MUTANTS = {
+    "nibble_order": ("(byte & 0x0F) : (byte >> 4)", "(byte >> 4) : (byte & 0x0F)"),
+    "offset_7": ("(double)(q - 8)", "(double)(q - 7)"),
+    "scale_index": ("scales[n * (K / 32) + k / 32]", "scales[n * (K / 32) + (k / 32 + 1) % (K / 32)]"),
+    "scale_per_16": ("scales[n * (K / 32) + k / 32]", "scales[n * (K / 32) + (k / 16) % (K / 32)]"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        const double t",
+                          "for (int64_t k = 0; k < K - 1; ++k) {\n        const double t"),
+    "flipped_sign": ("acc += t;", "acc -= t;"),
+    "wrong_row": ("one_output(xd + m * K,", "one_output(xd + ((m + 1) % M) * K,"),
+    "f16_bias": ("expo - 25)", "expo - 24)"),
+    "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "bf16_bias": ("expo - 134)", "expo - 133)"),
+    "pack_shift": ("(hi << 4)", "(hi << 3)"),
+    "abs_dropped": ("mag += fabs(t);", "mag += t;"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor for %s not unique in the oracle" % name
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.compile_library(str(mutated), lib_path)
+    lib = oracle.load_library(lib_path)
+    failures = []
+    for pin_name, pin in oracle_pins.ALL_PINS.items():
+        try:
+            pin(lib)
+        except AssertionError as e:
+            failures.append(pin_name)
+    assert failures, "planted mistake %r passed every pin" % name
