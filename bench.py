@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q4 linear layer on one MI355X.
+
+Workload: the Qwen2.5-7B-shaped projection set (q 3584x3584, k and v
+512x3584, gate and up 18944x3584, down 3584x18944), Q4 weights (blocks of 32,
+fp16 scales), bf16 activations, at every decode row count M = 1..8.  One
+step = the six projections at each M = 1..8 (48 calls through the library's
+crossover dispatcher), on a weight copy taken from a rotation pool larger than
+the 256 MB Infinity Cache, so weights stream from HBM.  Inputs are seeded
+synthetic data of those shapes (no trained weights); every input is resident
+in HBM before the timed region.
+
+Printed JSON line: value = achieved algorithmic HBM GB/s over the whole step
+(codes + scales + activations + outputs per call, divided by step time),
+with the dominant kernel's roofline and the fp64 CPU oracle timed on the
+host as a baseline.  The GEMV->GEMM crossover on the layer set and the
+per-M bandwidth are reported under "detail".
+
+Timing: each step's 48 launches are captured once in a HIP graph (one graph
+per pool copy); the timed region replays them between two events on the
+launch stream, after a barrier-free torch.cuda.synchronize() on both sides.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+
+
+def log(msg: str) -> None:
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--pool-gib", type=float, default=1.5, help="rotation pool of weight copies (GiB)")
+    ap.add_argument("--no-crossover", action="store_true", help="skip the GEMV/GEMM crossover sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--detail-json", default=None, help="also write the full results here")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_matmul_q4_amd as q4
+    import synth
+    from bit_quantized_matmul_q4_amd import build as hip_build
+
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mats = synth.SET_7B
+    Ms = list(range(1, 9))
+    set_bytes = sum(m.N * m.K // 2 + m.N * m.K // 16 for m in mats)
+    P = max(2, int(np.ceil(args.pool_gib * (1 << 30) / set_bytes)))
+    log("device %s, rotation pool %d copies of the layer set (%.2f GiB)"
+        % (torch.cuda.get_device_name(dev), P, P * set_bytes / (1 << 30)))
+
+    # ---- inputs, resident in HBM
+    base_w, base_s = [], []
+    for mi, m in enumerate(mats):
+        base_w.append(torch.from_numpy(synth.packed_codes(m.N, m.K, 3, mi)).to(dev))
+        base_s.append(torch.from_numpy(synth.scales(m.N, m.K, 3, mi).view(np.int16)).to(dev).view(torch.float16))
+    pool = [[(base_w[i].clone(), base_s[i].clone()) for i in range(len(mats))] for _ in range(P)]
+    del base_w, base_s
+    Mmax = 128
+    xs = {}
+    for K in sorted({m.K for m in mats}):
+        xb = synth.activations(Mmax, K, "bf16", 3, 100 + K)
+        xs[K] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    ys = {(mi, M): torch.empty((M, m.N), dtype=torch.float32, device=dev)
+          for mi, m in enumerate(mats) for M in range(1, Mmax + 1)
+          if M <= 16 or M in (20, 24, 32, 48, 64, 96, 124, 128)}
+    torch.cuda.synchronize()
+
+    def call(mi, M, p, kernel):
+        w, s = pool[p][mi]
+        q4.linear(xs[mats[mi].K][:M], w, s, out=ys[(mi, M)], kernel=kernel)
+
+    def capture(fn):
+        # warm the launch path (and any workspace) once outside capture
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graphs(graphs, reps):
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps  # ms
+
+    def step_bytes(M_list):
+        return sum(synth.algorithmic_bytes(M, m.N, m.K) for M in M_list for m in mats)
+
+    # ---- the step: 6 projections x M = 1..8, one graph per pool copy
+    log("capturing %d step graphs" % P)
+    step_graphs = [capture(lambda p=p: [call(mi, M, p, args.kernel) for M in Ms for mi in range(len(mats))])
+                   for p in range(P)]
+    for i in range(args.warmup):
+        step_graphs[i % P].replay()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    ms_step = time_graphs(step_graphs, args.steps)
+    bytes_step = step_bytes(Ms)
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    rows_per_s = sum(Ms) / (ms_step * 1e-3)
+    log("step %.3f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms_step * 1e3, value, 100 * value / PEAK_HBM_GBS))
+
+    # ---- per-launch durations of the dominant kernel (back-to-back launches
+    # of one shape over the pool, one graph) and per-M bandwidth
+    per_launch = {}
+    for M in Ms:
+        for mi in range(len(mats)):
+            g = capture(lambda M=M, mi=mi: [call(mi, M, p, args.kernel) for p in range(P)])
+            per_launch[(mi, M)] = time_graphs([g], 3) / P  # ms per launch
+    kern_ms = sum(per_launch.values())
+    achieved = bytes_step / (kern_ms * 1e-3) / 1e9
+    per_m = {}
+    for M in Ms:
+        t = sum(per_launch[(mi, M)] for mi in range(len(mats)))
+        per_m[str(M)] = round(step_bytes([M]) / (t * 1e-3) / 1e9, 1)
+    per_matrix_m8 = {mats[mi].name: round(synth.algorithmic_bytes(8, mats[mi].N, mats[mi].K)
+                                          / (per_launch[(mi, 8)] * 1e-3) / 1e9, 1) for mi in range(len(mats))}
+    log("per-M GB/s %s" % per_m)
+    log("per-matrix GB/s at M=8 %s" % per_matrix_m8)
+
+    # ---- GEMV -> GEMM crossover on the layer set
+    crossover = None
+    if not args.no_crossover:
+        cM = list(range(1, 17)) + [20, 24, 32, 48, 64, 96, 124, 128]
+        table = []
+        for M in cM:
+            t = {}
+            for kernel in ("gemv", "gemm"):
+                g = capture(lambda M=M, kernel=kernel: [call(mi, M, p % P, kernel)
+                                                        for p in range(4) for mi in range(len(mats))])
+                t[kernel] = time_graphs([g], 3) / 4 * 1e3  # us per layer set
+            table.append({"M": M, "gemv_us": round(t["gemv"], 2), "gemm_us": round(t["gemm"], 2),
+                          "gemm_over_gemv": round(t["gemm"] / t["gemv"], 3)})
+        mstar = next((r["M"] for r in table if r["gemm_us"] < r["gemv_us"]), None)
+        crossover = {"layer_set_table": table, "M_star": mstar,
+                     "T_rule": (mstar - 1) if mstar else None,
+                     "library_T": q4.get_crossover()}
+        log("crossover M* = %s" % mstar)
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+        oracle.load_library()
+        done_bytes, done_rows, t_cpu, sample = 0, 0, 0.0, []
+        x_host = {K: xs[K][:8].view(torch.int16).cpu().numpy().view(np.uint16) for K in xs}
+        w_host = [(pool[0][mi][0].cpu().numpy(), pool[0][mi][1].view(torch.int16).cpu().numpy().view(np.uint16))
+                  for mi in range(len(mats))]
+        for M in Ms:
+            for mi, m in enumerate(mats):
+                if t_cpu > args.cpu_seconds:
+                    break
+                t0 = time.perf_counter()
+                oracle.linear(x_host[m.K][:M], True, w_host[mi][0], w_host[mi][1])
+                t_cpu += time.perf_counter() - t0
+                done_bytes += synth.algorithmic_bytes(M, m.N, m.K)
+                done_rows += M
+                sample.append("%s@M=%d" % (m.name, M))
+        cpu = {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "%d of the step's 48 calls (%s ... %s), %.1f s" % (len(sample), sample[0], sample[-1], t_cpu),
+               "rows_per_s": round(done_rows / t_cpu, 2)}
+        log("cpu oracle %.3f GB/s on %d threads" % (cpu["value"], threads))
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) for Q4 linear at M=1..8, 7B shapes; crossover M",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Q4 codes uniform 0..15, fp16 scales |N(0,0.02)|, x ~ N(0,1) bf16)",
+        "config": {"workload": "qwen2.5-7b_layer_set_M1-8",
+                   "matrices": ["%s %dx%d" % (m.name, m.N, m.K) for m in mats],
+                   "M": Ms, "calls_per_step": len(Ms) * len(mats), "kernel": args.kernel,
+                   "rotation_pool_copies": P, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 1),
+                   "rows_per_s": round(rows_per_s, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "q4_gemv<bf16>", "launches_per_step": len(Ms) * len(mats),
+                     "avg_bytes_per_launch": int(bytes_step / (len(Ms) * len(mats))),
+                     "avg_launch_us": round(kern_ms / (len(Ms) * len(mats)) * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "crossover": crossover},
+    }
+    line = json.dumps(out)
+    if args.detail_json:
+        with open(args.detail_json, "w") as f:
+            f.write(json.dumps(out, indent=1) + "\n")
+    print(line)
+    sys.stdout.flush()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,190 @@
+// q4_api.cpp -- the C ABI of libq4.so (declared in include/q4.h).
+//
+// Argument checks, the crossover dispatcher and status codes.  The kernel
+// choice follows the row-count switch of "Why Continuous Batching Slowed
+// Down My LLM Inference Engine: A Metal Kernel Investigation" (section "Two
+// Rows of Input, Two Different Kernels": one row -> matrix-vector, more ->
+// matrix-matrix; section "Row-by-Row GEMV to the Rescue": the switch moved to
+// a measured threshold, <= 4 rows -> matrix-vector).  Here the threshold is
+// the crossover measured on MI355X, and because both kernels share one
+// reduction order the choice changes speed only, never the bits.
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/q4.h"
+#include "q4_launch.hpp"
+#include "q4_plan.hpp"
+
+namespace {
+
+// Measured GEMV -> GEMM crossover on MI355X (rows); M <= T runs the GEMV.
+constexpr int kDefaultCrossover = 16;
+
+thread_local int g_last_hip = 0;
+
+int env_int(const char *name, int fallback)
+{
+    const char *v = std::getenv(name);
+    if (!v || !*v)
+        return fallback;
+    char *end = nullptr;
+    const long r = std::strtol(v, &end, 10);
+    if (end == v || *end != '\0' || r < 0 || r > (1 << 30))
+        return fallback;
+    return (int)r;
+}
+
+std::atomic<int> &crossover()
+{
+    static std::atomic<int> t{env_int("Q4_CROSSOVER", kDefaultCrossover)};
+    return t;
+}
+
+// Q4_KERNEL=gemv|gemm forces a kernel for Q4_AUTO calls (read once).
+int forced_kernel()
+{
+    static const int k = [] {
+        const char *v = std::getenv("Q4_KERNEL");
+        if (v && std::strcmp(v, "gemv") == 0)
+            return (int)Q4_GEMV;
+        if (v && std::strcmp(v, "gemm") == 0)
+            return (int)Q4_GEMM;
+        return (int)Q4_AUTO;
+    }();
+    return k;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_shape(long long M, long long N, long long K)
+{
+    if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
+        return Q4_ERR_SHAPE;
+    // every element count must fit comfortably in 63 bits and every row
+    // index product used by the kernels in size_t
+    const long long lim = 1LL << 46;
+    if (M > lim / K || N > lim / K || M > lim / N)
+        return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return Q4_OK;
+    g_last_hip = (int)e;
+    return Q4_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+int q4_last_hip_error(void) { return g_last_hip; }
+
+const char *q4_strerror(int status)
+{
+    switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 32, K % 32 == 0, sizes in range)";
+    case Q4_ERR_ALIGN: return "misaligned pointer (x, Wq: 16 B; scales: 2 B; y: 4 B; workspace: 256 B)";
+    case Q4_ERR_ENUM: return "unknown dtype or kernel selector";
+    case Q4_ERR_HIP: return "HIP launch error (see q4_last_hip_error)";
+    case Q4_ERR_WORKSPACE: return "workspace_bytes > 0 with a NULL workspace";
+    default: return "unknown status";
+    }
+}
+
+int q4_get_crossover(void) { return crossover().load(std::memory_order_relaxed); }
+
+int q4_set_crossover(int T)
+{
+    if (T < 0)
+        return Q4_ERR_SHAPE;
+    crossover().store(T, std::memory_order_relaxed);
+    return Q4_OK;
+}
+
+int q4_segments(int K)
+{
+    if (K < 32 || K % 32 != 0)
+        return 0;
+    return q4::make_plan(K).S;
+}
+
+size_t q4_workspace_bytes(int M, int N, int K, int kernel)
+{
+    if (check_shape(M, N, K) != Q4_OK)
+        return 0;
+    int k = kernel;
+    if (k == Q4_AUTO)
+        k = forced_kernel() != Q4_AUTO ? forced_kernel() : (M <= q4_get_crossover() ? Q4_GEMV : Q4_GEMM);
+    if (k != Q4_GEMM)
+        return 0;
+    return q4::gemm_workspace_bytes(M, N, K);
+}
+
+int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales, float *y,
+                 int M, int N, int K, int kernel, void *workspace, size_t workspace_bytes,
+                 void *stream)
+{
+    if (!x || !Wq || !scales || !y)
+        return Q4_ERR_NULL;
+    if (x_dtype != Q4_F16 && x_dtype != Q4_BF16)
+        return Q4_ERR_ENUM;
+    if (kernel != Q4_AUTO && kernel != Q4_GEMV && kernel != Q4_GEMM)
+        return Q4_ERR_ENUM;
+    const int sh = check_shape(M, N, K);
+    if (sh != Q4_OK)
+        return sh;
+    if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(scales, 2) || !aligned(y, 4))
+        return Q4_ERR_ALIGN;
+    if (workspace_bytes > 0 && !workspace)
+        return Q4_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256))
+        return Q4_ERR_ALIGN;
+
+    int k = kernel;
+    if (k == Q4_AUTO)
+        k = forced_kernel() != Q4_AUTO ? forced_kernel() : (M <= q4_get_crossover() ? Q4_GEMV : Q4_GEMM);
+
+    const bool bf16 = x_dtype == Q4_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    if (k == Q4_GEMV)
+        return hip_status(q4::launch_gemv(x, bf16, (const uint8_t *)Wq, (const uint16_t *)scales, y,
+                                          M, N, K, s));
+    return hip_status(q4::launch_gemm(x, bf16, (const uint8_t *)Wq, (const uint16_t *)scales, y, M, N,
+                                      K, workspace_bytes ? workspace : nullptr, workspace_bytes, s));
+}
+
+int q4_linear(const void *x, const void *Wq, const void *scales, float *y, int M, int N, int K,
+              void *stream)
+{
+    return q4_linear_ex(x, Q4_BF16, Wq, scales, y, M, N, K, Q4_AUTO, nullptr, 0, stream);
+}
+
+int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y, int M, int N, int K,
+                  void *stream)
+{
+    return q4_linear_ex(x, Q4_F16, Wq, scales, y, M, N, K, Q4_AUTO, nullptr, 0, stream);
+}
+
+int q4_pack(const uint8_t *codes, uint8_t *Wq, int N, int K, void *stream)
+{
+    if (!codes || !Wq)
+        return Q4_ERR_NULL;
+    if (N < 1 || K < 32 || K % 32 != 0 || (long long)N * K > (1LL << 46))
+        return Q4_ERR_SHAPE;
+    if (!aligned(Wq, 16))
+        return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_pack(codes, Wq, N, K, (hipStream_t)stream));
+}
+
+}  // extern "C"

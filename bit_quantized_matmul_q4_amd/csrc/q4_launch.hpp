@@ -1,0 +1,26 @@
+// q4_launch.hpp -- host-side launchers exported by q4_kernels.hip to the C
+// ABI layer (q4_api.cpp).  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// Multi-row matrix-vector kernel: any M (rows are processed 16 at a time).
+hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
+                       float *y, int M, int N, int K, hipStream_t stream);
+
+// LDS-staged matrix-matrix kernel.  workspace may be NULL (no split of K
+// across workgroups); otherwise it holds workspace_bytes bytes.
+hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
+                       float *y, int M, int N, int K, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+// Bytes of workspace the matrix-matrix kernel can use for this shape.
+size_t gemm_workspace_bytes(int M, int N, int K);
+
+hipError_t launch_pack(const uint8_t *codes, uint8_t *wq, int N, int K, hipStream_t stream);
+
+}  // namespace q4

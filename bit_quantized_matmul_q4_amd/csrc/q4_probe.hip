@@ -1,0 +1,80 @@
+// q4_probe.hip -- probe kernels for the GPU tests (libq4probe.so).
+//
+// They run the library's own device primitives (q4_device.hpp) on raw lane
+// data so the tests can check, on the hardware, the assumptions the fixed
+// reduction order rests on: the MFMA operand / result lane layout, that an
+// MFMA result element depends only on its own A row and B column (not on its
+// slot or on other rows), run-to-run determinism, and the exactness of the
+// nibble dequantization.  Not part of the product library.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4_device.hpp"
+
+namespace {
+
+// One MFMA per wave: a, b are [waves][64 lanes][4 dwords], d is [waves][64][4].
+template <bool BF16>
+__global__ __launch_bounds__(64) void probe_mfma(const q4::u32x4 *a, const q4::u32x4 *b, q4::f32x4 *d)
+{
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    d[i] = q4::blockdot<BF16>(a[i], b[i]);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void probe_dequant(const uint32_t *w, q4::u32x4 *out, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        out[i] = q4::dequant8<BF16>(w[i]);
+}
+
+// fmaf(d, s, +0) on the VALU, for the single-rounding check of the scale step.
+__global__ __launch_bounds__(256) void probe_fma0(const float *d, const float *s, float *out, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        out[i] = __builtin_fmaf(d[i], s[i], 0.0f);
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4probe_mfma(const void *a, const void *b, void *d, int waves, int bf16, void *stream)
+{
+    if (!a || !b || !d || waves < 1)
+        return -1;
+    if (bf16)
+        hipLaunchKernelGGL(probe_mfma<true>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const q4::u32x4 *)b, (q4::f32x4 *)d);
+    else
+        hipLaunchKernelGGL(probe_mfma<false>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const q4::u32x4 *)b, (q4::f32x4 *)d);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int q4probe_dequant(const void *w, void *out, int n, int bf16, void *stream)
+{
+    if (!w || !out || n < 1)
+        return -1;
+    const dim3 grid((n + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL(probe_dequant<true>, grid, dim3(256), 0, (hipStream_t)stream,
+                           (const uint32_t *)w, (q4::u32x4 *)out, n);
+    else
+        hipLaunchKernelGGL(probe_dequant<false>, grid, dim3(256), 0, (hipStream_t)stream,
+                           (const uint32_t *)w, (q4::u32x4 *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int q4probe_fma0(const void *d, const void *s, void *out, int n, void *stream)
+{
+    if (!d || !s || !out || n < 1)
+        return -1;
+    hipLaunchKernelGGL(probe_fma0, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       (const float *)d, (const float *)s, (float *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+/*
+ * q4.h -- C ABI of libq4.so, the MI355X (gfx950) library for the 4-bit
+ * block-quantized linear layer of LLM decode:
+ *
+ *     y[M x N] = x[M x K] . dequant(Wq[N x K])^T
+ *
+ * The operation: "Why Continuous Batching Slowed Down My LLM Inference
+ * Engine: A Metal Kernel Investigation", section "Two Rows of Input, Two
+ * Different Kernels" -- a 4-bit quantized weight matrix applied to one input
+ * row (matrix-vector kernel) or to several rows at once (matrix-matrix
+ * kernel), where the rows are token positions of a batching step (section
+ * "The Other Request Already Finished").  That page also shows why a row's
+ * result must not depend on which kernel ran (sections "Same Prompt,
+ * Different Story" and "The Other Request Already Finished"): this library
+ * makes every output row bit-identical whatever M is and whichever kernel
+ * runs.
+ *
+ * Weight format (the pages say only "4-bit quantized"; the library fixes):
+ *   - blocks of 32 consecutive weights along K; one IEEE binary16 scale d
+ *     per block; 4-bit codes q in 0..15; weight value (q - 8) * d;
+ *   - Wq: uint8 [N][K/2], row-major; byte j of row n holds the code of
+ *     k = 2j in bits 0..3 and of k = 2j+1 in bits 4..7;
+ *   - scales: binary16 [N][K/32], row-major (zero and subnormal scales are
+ *     legal and used exactly; inf/nan scales are outside the contract).
+ * Activations x: [M][K] row-major, bfloat16 (q4_linear) or binary16
+ * (q4_linear_f16).  Output y: float32 [M][N] row-major, overwritten (no
+ * bias, no accumulation into y).
+ *
+ * Pointers passed to the compute calls are DEVICE pointers (memory of the
+ * current HIP device).  `stream` is a hipStream_t cast to void* (NULL = the
+ * null stream).  Every call only enqueues work on `stream` and returns; it
+ * never synchronizes, allocates, frees or retains memory.  The caller owns
+ * every buffer.  Aliasing y (or the workspace) with any input is undefined.
+ * Calls are thread-safe; the only global state is the crossover threshold.
+ *
+ * Return value: Q4_OK (0) or a negative status.  Argument checks run before
+ * any HIP call, so a failed check launches nothing.  Q4_ERR_HIP keeps the
+ * HIP error code, readable through q4_last_hip_error() on the same thread.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+
+enum q4_status {
+    Q4_OK = 0,
+    Q4_ERR_NULL = -1,      /* a required pointer is NULL */
+    Q4_ERR_SHAPE = -2,     /* M < 1, N < 1, K < 32, K % 32 != 0, or a size overflows */
+    Q4_ERR_ALIGN = -3,     /* x or Wq not 16-byte aligned, scales not 2-byte aligned,
+                              y not 4-byte aligned */
+    Q4_ERR_ENUM = -4,      /* unknown dtype or kernel selector */
+    Q4_ERR_HIP = -5,       /* a HIP call failed (see q4_last_hip_error) */
+    Q4_ERR_WORKSPACE = -6  /* workspace_bytes non-zero with a NULL workspace */
+};
+
+enum q4_dtype { Q4_F16 = 0, Q4_BF16 = 1 };
+
+enum q4_kernel {
+    Q4_AUTO = 0, /* matrix-vector kernel if M <= crossover, else matrix-matrix */
+    Q4_GEMV = 1, /* force the multi-row matrix-vector kernel (any M) */
+    Q4_GEMM = 2  /* force the LDS-staged matrix-matrix (MFMA tile) kernel */
+};
+
+/*
+ * y = x . dequant(Wq)^T with bfloat16 activations.
+ *   x      bf16  [M][K]      device, 16-byte aligned
+ *   Wq     uint8 [N][K/2]    device, 16-byte aligned
+ *   scales fp16  [N][K/32]   device, 2-byte aligned
+ *   y      fp32  [M][N]      device, 4-byte aligned, overwritten
+ * Kernel chosen by the crossover rule (Q4_AUTO), with no workspace.
+ */
+int q4_linear(const void *x, const void *Wq, const void *scales, float *y,
+              int M, int N, int K, void *stream);
+
+/* Same as q4_linear with binary16 activations. */
+int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y,
+                  int M, int N, int K, void *stream);
+
+/*
+ * Full form.  x_dtype is Q4_BF16 or Q4_F16; kernel is a q4_kernel value.
+ * workspace: optional device scratch of workspace_bytes bytes (256-byte
+ * aligned) that lets the matrix-matrix kernel split K across workgroups;
+ * pass NULL and 0 to run without it (same bits, fewer workgroups).
+ * q4_workspace_bytes() gives the size that enables the full split for a
+ * shape.  A workspace smaller than that is used for a smaller split.
+ * Two calls that share one workspace must not overlap in time.
+ */
+int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
+                 float *y, int M, int N, int K, int kernel,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes that q4_linear_ex can use for this shape and kernel
+ * (0 if the kernel uses none).  Pure host computation; 0 for bad shapes. */
+size_t q4_workspace_bytes(int M, int N, int K, int kernel);
+
+/*
+ * Pack 4-bit codes: codes uint8 [N][K] (only bits 0..3 of each byte are
+ * used) -> Wq uint8 [N][K/2] with the nibble order above.  Device pointers;
+ * codes any alignment, Wq 16-byte aligned; K must be a positive multiple of
+ * 32.  Bit-exact; scales are not touched (they pass through unchanged).
+ */
+int q4_pack(const uint8_t *codes, uint8_t *Wq, int N, int K, void *stream);
+
+/* Crossover threshold T: Q4_AUTO uses the matrix-vector kernel iff M <= T.
+ * Initialised from the environment variable Q4_CROSSOVER if set, else the
+ * measured default.  q4_set_crossover returns Q4_ERR_SHAPE for T < 0.
+ * The threshold never changes results, only speed. */
+int q4_get_crossover(void);
+int q4_set_crossover(int T);
+
+/* Number of K-segments the fixed reduction order uses for this K (1..16),
+ * or 0 if K is not a positive multiple of 32.  It depends on K only. */
+int q4_segments(int K);
+
+/* Human-readable text for a status code (static storage). */
+const char *q4_strerror(int status);
+
+/* HIP error code of the last Q4_ERR_HIP on the calling thread (0 if none). */
+int q4_last_hip_error(void);
+
+/* Q4_ABI_VERSION of the loaded library. */
+int q4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

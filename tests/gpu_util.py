@@ -1,0 +1,109 @@
+"""Helpers shared by the GPU tests: build-if-missing, host<->device moves of
+raw bit patterns, and the oracle comparison."""
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+
+import numpy as np
+import torch
+
+import bit_quantized_matmul_q4_amd as q4
+from bit_quantized_matmul_q4_amd import _lib, build
+
+DEV = torch.device("cuda:0")
+
+# max |y_gpu - y_ref| / sum|x w| allowed against the fp64 oracle
+TOL = 2e-3
+
+
+def ensure_built() -> None:
+    """Tests call the in-tree build; they build only when nothing is built."""
+    if not os.path.exists(build.LIB):
+        build.build_library()
+    if not os.path.exists(build.PROBE_LIB):
+        build.build_probe()
+
+
+def require_gpu() -> None:
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    ensure_built()
+    _lib.load()
+
+
+def note(msg: str) -> None:
+    """Name the case before a GPU step (flushed, so it survives a crash)."""
+    sys.stdout.write("[gpu] %s\n" % msg)
+    sys.stdout.flush()
+
+
+def x_to_dev(bits: np.ndarray, bf16: bool) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).to(DEV)
+    return t.view(torch.bfloat16 if bf16 else torch.float16)
+
+
+def scales_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).to(DEV).view(torch.float16)
+
+
+def u8_to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEV)
+
+
+def y_bits(y: torch.Tensor) -> np.ndarray:
+    return y.detach().cpu().numpy().view(np.uint32)
+
+
+def run_linear(x_bits, bf16, wq, s_bits, kernel="auto", workspace=True) -> torch.Tensor:
+    out = q4.linear(x_to_dev(x_bits, bf16), u8_to_dev(wq), scales_to_dev(s_bits), kernel=kernel,
+                    workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+class Probe:
+    """libq4probe.so: raw-lane probes of the library's device primitives."""
+
+    def __init__(self):
+        ensure_built()
+        self.lib = ctypes.CDLL(build.PROBE_LIB)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        self.lib.q4probe_mfma.argtypes = [vp, vp, vp, i, i, vp]
+        self.lib.q4probe_dequant.argtypes = [vp, vp, i, i, vp]
+        self.lib.q4probe_fma0.argtypes = [vp, vp, vp, i, vp]
+
+    def mfma(self, a_lanes: np.ndarray, b_lanes: np.ndarray, bf16: bool) -> np.ndarray:
+        """a_lanes, b_lanes: uint16 [waves, 64, 8] -> float32 [waves, 64, 4]."""
+        waves = a_lanes.shape[0]
+        a = torch.from_numpy(np.ascontiguousarray(a_lanes, np.uint16).view(np.int16)).to(DEV)
+        b = torch.from_numpy(np.ascontiguousarray(b_lanes, np.uint16).view(np.int16)).to(DEV)
+        d = torch.empty((waves, 64, 4), dtype=torch.float32, device=DEV)
+        rc = self.lib.q4probe_mfma(a.data_ptr(), b.data_ptr(), d.data_ptr(), waves, int(bf16),
+                                   torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        return d.cpu().numpy()
+
+    def dequant(self, words: np.ndarray, bf16: bool) -> np.ndarray:
+        """uint32 [n] -> uint16 [n, 8] operand values."""
+        n = words.shape[0]
+        w = torch.from_numpy(np.ascontiguousarray(words, np.uint32).view(np.int32)).to(DEV)
+        out = torch.empty((n, 4), dtype=torch.int32, device=DEV)
+        rc = self.lib.q4probe_dequant(w.data_ptr(), out.data_ptr(), n, int(bf16),
+                                      torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint16).reshape(n, 8)
+
+    def fma0(self, d: np.ndarray, s: np.ndarray) -> np.ndarray:
+        n = d.shape[0]
+        dt = torch.from_numpy(np.ascontiguousarray(d, np.float32)).to(DEV)
+        st = torch.from_numpy(np.ascontiguousarray(s, np.float32)).to(DEV)
+        out = torch.empty(n, dtype=torch.float32, device=DEV)
+        rc = self.lib.q4probe_fma0(dt.data_ptr(), st.data_ptr(), out.data_ptr(), n,
+                                   torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        return out.cpu().numpy()

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports every function the
+header declares, and its host logic (argument checks, the segment schedule,
+workspace sizing, the crossover setting) behaves as documented.  No call here
+reaches a kernel launch: every compute call fails its argument checks, which
+run before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_matmul_q4_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from bit_quantized_matmul_q4_amd import build
+        build.build_library()
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), "libq4.so does not export %s" % name
+    assert sorted(names) == sorted(_lib.EXPORTS)
+
+
+def test_abi_and_strerror(lib):
+    assert lib.q4_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
+    assert lib.q4_strerror(-99) == b"unknown status"
+    assert lib.q4_last_hip_error() == 0
+
+
+def plan(K):
+    """The K-segment schedule, restated from its definition: quads of four
+    blocks, S = min(16, largest power of two <= number of quads)."""
+    nb = K // 32
+    G = (nb + 3) // 4
+    S = 1
+    while S * 2 <= G and S < 16:
+        S *= 2
+    segs = [(4 * (j * G // S), min(nb, 4 * ((j + 1) * G // S))) for j in range(S)]
+    return nb, G, S, segs
+
+
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 256, 512, 896, 2048, 3584, 4864, 18944, 32 * 997])
+def test_segments(lib, K):
+    nb, G, S, segs = plan(K)
+    assert lib.q4_segments(K) == S
+    # segments tile the blocks in order, none empty, all starting on a quad
+    assert segs[0][0] == 0 and segs[-1][1] == nb
+    for (a, b), (c, _) in zip(segs, segs[1:]):
+        assert b == c
+    assert all(b > a and a % 4 == 0 for a, b in segs)
+
+
+def test_segments_bad_k(lib):
+    for K in (0, 16, 31, 33, -32):
+        assert lib.q4_segments(K) == 0
+
+
+def test_crossover_get_set(lib):
+    old = lib.q4_get_crossover()
+    try:
+        assert lib.q4_set_crossover(7) == 0
+        assert lib.q4_get_crossover() == 7
+        assert lib.q4_set_crossover(-1) == _lib.Q4_ERR_SHAPE
+        assert lib.q4_get_crossover() == 7
+    finally:
+        lib.q4_set_crossover(old)
+
+
+def test_workspace_bytes(lib):
+    assert lib.q4_workspace_bytes(8, 3584, 3584, _lib.Q4_GEMV) == 0
+    ws = lib.q4_workspace_bytes(124, 3584, 3584, _lib.Q4_GEMM)
+    assert ws > 0 and ws % (124 * 3584 * 4) == 0
+    gk = ws // (124 * 3584 * 4)
+    assert gk & (gk - 1) == 0 and gk <= 16
+    assert lib.q4_workspace_bytes(0, 16, 32, _lib.Q4_GEMM) == 0   # bad shape
+    assert lib.q4_workspace_bytes(4, 16, 48, _lib.Q4_GEMM) == 0   # bad shape
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (checks fail first)
+
+
+def call(lib, x=FAKE, dt=_lib.Q4_BF16, w=FAKE, s=FAKE, y=FAKE, M=4, N=16, K=64,
+         kern=_lib.Q4_AUTO, ws=None, wsb=0):
+    return lib.q4_linear_ex(x, dt, w, s, y, M, N, K, kern, ws, wsb, None)
+
+
+def test_argument_checks(lib):
+    assert call(lib, x=None) == _lib.Q4_ERR_NULL
+    assert call(lib, w=None) == _lib.Q4_ERR_NULL
+    assert call(lib, s=None) == _lib.Q4_ERR_NULL
+    assert call(lib, y=None) == _lib.Q4_ERR_NULL
+    assert call(lib, dt=2) == _lib.Q4_ERR_ENUM
+    assert call(lib, kern=3) == _lib.Q4_ERR_ENUM
+    assert call(lib, kern=-1) == _lib.Q4_ERR_ENUM
+    for M, N, K in ((0, 16, 64), (4, 0, 64), (4, 16, 0), (4, 16, 48), (4, 16, 16), (-1, 16, 64),
+                    (1 << 30, 1 << 30, 32)):
+        assert call(lib, M=M, N=N, K=K) == _lib.Q4_ERR_SHAPE, (M, N, K)
+    assert call(lib, x=FAKE + 2) == _lib.Q4_ERR_ALIGN
+    assert call(lib, w=FAKE + 8) == _lib.Q4_ERR_ALIGN
+    assert call(lib, s=FAKE + 1) == _lib.Q4_ERR_ALIGN
+    assert call(lib, y=FAKE + 2) == _lib.Q4_ERR_ALIGN
+    assert call(lib, ws=None, wsb=64) == _lib.Q4_ERR_WORKSPACE
+    assert call(lib, ws=FAKE + 16, wsb=64) == _lib.Q4_ERR_ALIGN
+    # the short forms run the same checks
+    assert lib.q4_linear(None, FAKE, FAKE, FAKE, 1, 16, 64, None) == _lib.Q4_ERR_NULL
+    assert lib.q4_linear_f16(FAKE, FAKE, FAKE, FAKE, 1, 16, 40, None) == _lib.Q4_ERR_SHAPE
+    assert lib.q4_pack(None, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert lib.q4_pack(FAKE, FAKE, 4, 40, None) == _lib.Q4_ERR_SHAPE
+    assert lib.q4_pack(FAKE, FAKE + 4, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert lib.q4_last_hip_error() == 0

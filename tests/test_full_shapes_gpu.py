@@ -1,0 +1,69 @@
+"""Full-size 7B-shaped matrices, in the launch configuration the benchmark
+times: outputs sampled against the oracle (which computes them one by one),
+plus the bit contract between the kernels at full size."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_matmul_q4_amd as q4
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = 1500
+
+
+def sampled_check(x_bits, wq, s_bits, y, rng, bf16=True):
+    M, N = y.shape
+    ms = rng.integers(0, M, SAMPLES)
+    ns = rng.integers(0, N, SAMPLES)
+    # always include the corners (tails of both dimensions)
+    ms = np.concatenate([ms, [0, M - 1, 0, M - 1]])
+    ns = np.concatenate([ns, [0, 0, N - 1, N - 1]])
+    y_ref, a_ref = oracle.linear_sampled(x_bits, bf16, wq, s_bits, ms, ns)
+    err = oracle.max_normalised_error(y[ms, ns], y_ref, a_ref)
+    assert err <= gu.TOL, err
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    gu.require_gpu()
+
+
+@pytest.mark.parametrize("mi", range(6))
+def test_7b_layer_set(mi):
+    mat = synth.SET_7B[mi]
+    rng = np.random.default_rng(40 + mi)
+    x, codes, s = synth.problem(mat.N, mat.K, 124, "bf16", workload=3, matrix=mi)
+    wq = oracle.pack(codes)
+    xd, wd, sd = gu.x_to_dev(x, True), gu.u8_to_dev(wq), gu.scales_to_dev(s)
+    gu.note("7B %s M=8 gemv" % mat.name)
+    y8 = q4.linear(xd[:8], wd, sd, kernel="gemv")
+    torch.cuda.synchronize()
+    y8h = y8.cpu().numpy()
+    sampled_check(x[:8], wq, s, y8h, rng)
+    for M in (1, 3, 8, 16, 124):
+        for kernel in ("auto", "gemv", "gemm"):
+            gu.note("7B %s M=%d %s" % (mat.name, M, kernel))
+            y = q4.linear(xd[:M], wd, sd, kernel=kernel).cpu().numpy()
+            assert np.array_equal(y[: min(M, 8)].view(np.uint32), y8h[: min(M, 8)].view(np.uint32))
+            if M == 124:
+                sampled_check(x[:124], wq, s, y, rng)
+
+
+def test_lm_head_sampled():
+    mat = synth.LM_HEAD_7B
+    rng = np.random.default_rng(50)
+    x = synth.activations(64, mat.K, "bf16", workload=5, matrix=6)
+    wq = synth.packed_codes(mat.N, mat.K, workload=5, matrix=6)
+    s = synth.scales(mat.N, mat.K, workload=5, matrix=6)
+    xd, wd, sd = gu.x_to_dev(x, True), gu.u8_to_dev(wq), gu.scales_to_dev(s)
+    ys = {}
+    for M in (1, 4, 16, 64):
+        gu.note("lm_head M=%d" % M)
+        ys[M] = q4.linear(xd[:M], wd, sd).cpu().numpy()
+        sampled_check(x[:M], wq, s, ys[M], rng)
+    for M in (1, 4, 16):
+        assert np.array_equal(ys[64][:M].view(np.uint32), ys[M].view(np.uint32))

@@ -1,0 +1,138 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI.
+
+Tolerance: max |y_gpu - y_ref| / A <= 2e-3 with A = sum_k |x w| (the bound
+the library promises); the expected error of the fixed reduction order is
+about 1e-6.  Bit-exact where every partial sum is representable (one-hot
+read-out, the exact regime, the hand-worked example)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+from tests import oracle_pins
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    gu.require_gpu()
+
+
+def check(x_bits, bf16, codes, s_bits, kernel, tol=gu.TOL):
+    wq = oracle.pack(codes)
+    y = gu.run_linear(x_bits, bf16, wq, s_bits, kernel=kernel).cpu().numpy()
+    y_ref, a_ref = oracle.linear(x_bits, bf16, wq, s_bits)
+    err = oracle.max_normalised_error(y, y_ref, a_ref)
+    assert err <= tol, "normalised error %.3g > %.3g" % (err, tol)
+    return y, y_ref, a_ref
+
+
+KERNELS = ["gemv", "gemm", "auto"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_hand_example_exact(kernel):
+    gu.note("hand example kernel=%s" % kernel)
+    g, xv, codes, scales, packed = oracle_pins.hand_example_inputs()
+    y_exp = np.array([float(v) for v in g["y"]], np.float32)
+    for bf16 in (True, False):
+        xb = synth.f64_to_bf16_bits(xv) if bf16 else synth.f64_to_f16_bits(xv)
+        y = gu.run_linear(xb, bf16, packed, scales, kernel=kernel).cpu().numpy()
+        assert np.array_equal(y[:, 0], y_exp), (kernel, bf16, y[:, 0])
+
+
+# (M, N, K, bf16): several tiles, ragged N and M tails, K with a short last
+# quad, the smallest K, segment counts 1..16
+SHAPES = [
+    (1, 896, 896, False), (2, 128, 896, False), (4, 4864, 896, False), (3, 896, 4864, False),
+    (1, 16, 32, True), (5, 17, 64, True), (16, 40, 96, True), (17, 33, 160, True),
+    (8, 100, 32 * 37, True), (7, 512, 3584, True), (33, 70, 1024, True), (64, 64, 2048, False),
+    (100, 130, 640, True), (124, 48, 3584, True), (128, 96, 256, False), (9, 1, 32 * 67, True),
+]
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+@pytest.mark.parametrize("M,N,K,bf16", SHAPES)
+def test_parity_random(M, N, K, bf16, kernel):
+    gu.note("parity M=%d N=%d K=%d bf16=%s kernel=%s" % (M, N, K, bf16, kernel))
+    x, codes, s = synth.problem(N, K, M, "bf16" if bf16 else "f16", workload=91, matrix=N * 7 + K)
+    check(x, bf16, codes, s, kernel)
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_one_hot_readout_exact(kernel, bf16):
+    """x = e_k reads out (q[n][k] - 8) d[n][k/32] exactly for every k."""
+    gu.note("one-hot kernel=%s bf16=%s" % (kernel, bf16))
+    rng = np.random.default_rng(21)
+    N, K = 40, 128
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = oracle_pins.random_scale_bits(rng, (N, K // 32))
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80 if bf16 else 0x3C00
+    wq = oracle.pack(codes)
+    y = gu.run_linear(x, bf16, wq, s, kernel=kernel).cpu().numpy()
+    y_ref, _ = oracle.linear(x, bf16, wq, s)
+    assert np.array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+@pytest.mark.parametrize("K", [32, 3584, 18944])
+def test_exact_regime(kernel, K):
+    """Integer x in [-4, 4], scales 2^-1..2^-4: every block sum is an integer
+    and every partial a multiple of 2^-4 below 2^19, so all are exact."""
+    gu.note("exact regime kernel=%s K=%d" % (kernel, K))
+    rng = np.random.default_rng(22 + K)
+    M, N = 6, 48
+    x = synth.f64_to_bf16_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float64))
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = synth.f64_to_f16_bits(2.0 ** -rng.integers(1, 5, size=(N, K // 32)))
+    wq = oracle.pack(codes)
+    y = gu.run_linear(x, True, wq, s, kernel=kernel).cpu().numpy()
+    y_ref, _ = oracle.linear(x, True, wq, s)
+    assert np.array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+def test_special_cases(kernel):
+    gu.note("special cases kernel=%s" % kernel)
+    rng = np.random.default_rng(23)
+    M, N, K = 5, 37, 256
+    x = synth.activations(M, K, "bf16", workload=92)
+    s = synth.scales(N, K, workload=92)
+    # all codes 8 -> zeros
+    y = gu.run_linear(x, True, oracle.pack(np.full((N, K), 8, np.uint8)), s, kernel=kernel)
+    assert (y == 0).all()
+    # zero input -> zeros
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    y = gu.run_linear(np.zeros((M, K), np.uint16), True, oracle.pack(codes), s, kernel=kernel)
+    assert (y == 0).all()
+    # single block: y = fl(d * s) with s exact
+    xk = synth.f64_to_bf16_bits(rng.integers(-3, 4, size=(M, 32)).astype(np.float64))
+    y = gu.run_linear(xk, True, oracle.pack(codes[:, :32]), s[:, :1], kernel=kernel).cpu().numpy()
+    y_ref, _ = oracle.linear(xk, True, oracle.pack(codes[:, :32]), s[:, :1])
+    assert np.array_equal(y, y_ref.astype(np.float32))
+    # subnormal and zero scales, random bit-pattern activations
+    s2 = oracle_pins.random_scale_bits(rng, (N, K // 32))
+    x2 = oracle_pins.random_finite_bits(rng, (M, K), bf16=False)
+    check(x2, False, codes, s2, kernel)
+
+
+@pytest.mark.parametrize("workload", [1, 2])
+def test_small_workloads_full(workload):
+    """The 0.5B-shaped workloads, every matrix and every M, both kernels."""
+    spec = synth.WORKLOADS[workload]
+    bf16 = spec["x"] == "bf16"
+    for mi, mat in enumerate(spec["matrices"]):
+        Mmax = max(spec["Ms"])
+        x, codes, s = synth.problem(mat.N, mat.K, Mmax, spec["x"], workload, mi)
+        wq = oracle.pack(codes)
+        y_ref, a_ref = oracle.linear(x, bf16, wq, s)
+        for M in spec["Ms"]:
+            for kernel in ("auto", "gemv", "gemm"):
+                gu.note("workload %d %s M=%d kernel=%s" % (workload, mat.name, M, kernel))
+                y = gu.run_linear(x[:M], bf16, wq, s, kernel=kernel).cpu().numpy()
+                err = oracle.max_normalised_error(y, y_ref[:M], a_ref[:M])
+                assert err <= gu.TOL, (mat.name, M, kernel, err)
