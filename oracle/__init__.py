@@ -15,7 +15,9 @@ Two Different Kernels" (each weight row is dot-producted with each input row):
 
 with the block format stated in ``q4_oracle.c``.  Inputs are raw bit
 patterns: x as uint16 (fp16 or bf16 bits), scales as uint16 (fp16 bits),
-packed codes as uint8.
+packed codes as uint8.  Weights come in the canonical row-major layout
+(``linear``) or in the library's tiled layout (``linear_tiled``); both are
+defined in ``q4_oracle.c``.
 """
 from __future__ import annotations
 
@@ -61,9 +63,20 @@ def _declare(lib):
     lib.q4o_unpack.restype = None
     lib.q4o_linear.argtypes = [u16p, ctypes.c_int, u8p, u16p, i64, i64, i64, f64p, f64p]
     lib.q4o_linear.restype = ctypes.c_int
-    lib.q4o_linear_sampled.argtypes = [u16p, ctypes.c_int, u8p, u16p, i64, i64, i64,
+    lib.q4o_linear_fmt.argtypes = [u16p, ctypes.c_int, u8p, u16p, i64, i64, i64, ctypes.c_int,
+                                   f64p, f64p]
+    lib.q4o_linear_fmt.restype = ctypes.c_int
+    lib.q4o_linear_sampled.argtypes = [u16p, ctypes.c_int, u8p, u16p, i64, i64, i64, ctypes.c_int,
                                        i64p, i64p, i64, f64p, f64p]
     lib.q4o_linear_sampled.restype = ctypes.c_int
+    lib.q4o_tiled_code_bytes.argtypes = [i64, i64]
+    lib.q4o_tiled_code_bytes.restype = i64
+    lib.q4o_tiled_scale_count.argtypes = [i64, i64]
+    lib.q4o_tiled_scale_count.restype = i64
+    lib.q4o_pack_tiled.argtypes = [u8p, u16p, u8p, u16p, i64, i64]
+    lib.q4o_pack_tiled.restype = None
+    lib.q4o_unpack_tiled.argtypes = [u8p, u16p, u8p, u16p, i64, i64]
+    lib.q4o_unpack_tiled.restype = None
     return lib
 
 
@@ -120,6 +133,44 @@ def unpack(wq: np.ndarray, K: int, lib=None) -> np.ndarray:
     return out
 
 
+def tiled_sizes(N: int, K: int, lib=None):
+    """(code bytes, scale entries) of the tiled layout for an N x K matrix."""
+    lib = lib or load_library()
+    return int(lib.q4o_tiled_code_bytes(N, K)), int(lib.q4o_tiled_scale_count(N, K))
+
+
+def pack_tiled(codes: np.ndarray, scales: np.ndarray, lib=None):
+    """codes uint8 [N, K] (low 4 bits used), scales fp16 bits [N, K/32] ->
+    (tiled codes uint8 [bytes], tiled scales uint16 [entries])."""
+    lib = lib or load_library()
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    N, K = codes.shape
+    if K % 32 or scales.shape != (N, K // 32):
+        raise ValueError("need K % 32 == 0 and scales [N, K/32]")
+    nb, ns = tiled_sizes(N, K, lib)
+    wq = np.empty(nb, np.uint8)
+    sc = np.empty(ns, np.uint16)
+    lib.q4o_pack_tiled(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint16),
+                       _ptr(wq, ctypes.c_uint8), _ptr(sc, ctypes.c_uint16), N, K)
+    return wq, sc
+
+
+def unpack_tiled(wq_t: np.ndarray, sc_t: np.ndarray, N: int, K: int, lib=None):
+    """Inverse of pack_tiled -> (codes uint8 [N, K], scales uint16 [N, K/32])."""
+    lib = lib or load_library()
+    nb, ns = tiled_sizes(N, K, lib)
+    wq_t = _c(wq_t, np.uint8).reshape(-1)
+    sc_t = _c(sc_t, np.uint16).reshape(-1)
+    if wq_t.size != nb or sc_t.size != ns:
+        raise ValueError("tiled sizes for (%d, %d) are %d code bytes and %d scales" % (N, K, nb, ns))
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint16)
+    lib.q4o_unpack_tiled(_ptr(wq_t, ctypes.c_uint8), _ptr(sc_t, ctypes.c_uint16),
+                         _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint16), N, K)
+    return codes, scales
+
+
 def _check(x_bits, wq, scales):
     x_bits = _c(x_bits, np.uint16)
     wq = _c(wq, np.uint8)
@@ -134,7 +185,7 @@ def _check(x_bits, wq, scales):
 
 
 def linear(x_bits: np.ndarray, x_is_bf16: bool, wq: np.ndarray, scales: np.ndarray, lib=None):
-    """Full fp64 product.  Returns (y, A), both float64 [M, N]."""
+    """Full fp64 product, canonical layout.  Returns (y, A), both float64 [M, N]."""
     x_bits, wq, scales, M, N, K = _check(x_bits, wq, scales)
     y = np.empty((M, N), np.float64)
     a = np.empty((M, N), np.float64)
@@ -146,18 +197,52 @@ def linear(x_bits: np.ndarray, x_is_bf16: bool, wq: np.ndarray, scales: np.ndarr
     return y, a
 
 
-def linear_sampled(x_bits, x_is_bf16, wq, scales, ms, ns, lib=None):
-    """Outputs (ms[i], ns[i]) only.  Returns (y, A), float64 [count]."""
-    x_bits, wq, scales, M, N, K = _check(x_bits, wq, scales)
+def _check_tiled(x_bits, wq_t, sc_t, N, K, lib):
+    x_bits = _c(x_bits, np.uint16)
+    M = x_bits.shape[0]
+    if x_bits.shape[1] != K or K % 32 or K <= 0:
+        raise ValueError("x must be [M, K] with K a positive multiple of 32")
+    nb, ns = tiled_sizes(N, K, lib)
+    wq_t = _c(wq_t, np.uint8).reshape(-1)
+    sc_t = _c(sc_t, np.uint16).reshape(-1)
+    if wq_t.size != nb or sc_t.size != ns:
+        raise ValueError("tiled sizes for (%d, %d) are %d code bytes and %d scales" % (N, K, nb, ns))
+    return x_bits, wq_t, sc_t, M
+
+
+def linear_tiled(x_bits, x_is_bf16, wq_t, sc_t, N: int, K: int, lib=None):
+    """Full fp64 product from the tiled layout.  Returns (y, A) [M, N]."""
+    lib = lib or load_library()
+    x_bits, wq_t, sc_t, M = _check_tiled(x_bits, wq_t, sc_t, N, K, lib)
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    rc = lib.q4o_linear_fmt(_ptr(x_bits, ctypes.c_uint16), int(bool(x_is_bf16)), _ptr(wq_t, ctypes.c_uint8),
+                            _ptr(sc_t, ctypes.c_uint16), M, N, K, 1, _ptr(y, ctypes.c_double),
+                            _ptr(a, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oracle q4o_linear_fmt failed (%d)" % rc)
+    return y, a
+
+
+def linear_sampled(x_bits, x_is_bf16, wq, scales, ms, ns, lib=None, tiled_nk=None):
+    """Outputs (ms[i], ns[i]) only.  Returns (y, A), float64 [count].
+    tiled_nk=(N, K) reads wq/scales in the tiled layout."""
+    lib = lib or load_library()
+    if tiled_nk is not None:
+        N, K = tiled_nk
+        x_bits, wq, scales, M = _check_tiled(x_bits, wq, scales, N, K, lib)
+    else:
+        x_bits, wq, scales, M, N, K = _check(x_bits, wq, scales)
     ms = _c(ms, np.int64)
     ns = _c(ns, np.int64)
     if ms.shape != ns.shape or ms.ndim != 1:
         raise ValueError("ms and ns must be 1-D of equal length")
     y = np.empty(ms.shape[0], np.float64)
     a = np.empty(ms.shape[0], np.float64)
-    rc = (lib or load_library()).q4o_linear_sampled(
+    rc = lib.q4o_linear_sampled(
         _ptr(x_bits, ctypes.c_uint16), int(bool(x_is_bf16)), _ptr(wq, ctypes.c_uint8),
-        _ptr(scales, ctypes.c_uint16), M, N, K, _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64),
+        _ptr(scales, ctypes.c_uint16), M, N, K, int(tiled_nk is not None),
+        _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64),
         ms.shape[0], _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
     if rc != 0:
         raise RuntimeError("oracle q4o_linear_sampled failed (%d)" % rc)

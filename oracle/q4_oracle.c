@@ -20,9 +20,17 @@
  *   - The pages do not fix a 4-bit format.  The format used here: blocks of
  *     32 consecutive weights along K share one IEEE binary16 scale d; each
  *     weight has a code q in 0..15; the weight's value is (q - 8) * d.
- *     Packed layout: row n of Wq holds K/2 bytes; byte j holds the code of
- *     k = 2j in bits 0..3 and the code of k = 2j+1 in bits 4..7.  Scales
- *     are row-major [N][K/32].
+ *     Canonical packed layout: row n of Wq holds K/2 bytes; byte j holds the
+ *     code of k = 2j in bits 0..3 and the code of k = 2j+1 in bits 4..7.
+ *     Scales are row-major [N][K/32].
+ *   - The library's tiled layout (what its pack produces and its kernels
+ *     read): tiles of 16 rows (t = n / 16, c = n % 16) by 4 blocks
+ *     (q = b / 4, i = b % 4), ordered [ceil(N/16)][ceil(nb/4)], 1024 code
+ *     bytes and 64 scales each.  Inside a code tile, the byte at
+ *     16 * (16 g + c) + 4 i + j is canonical byte 4 g + j of block b of row
+ *     n (the codes of k = 32 b + 8 g + 2 j and k + 1, g, j in 0..3).  The
+ *     scale of (n, b) is element 4 c + i of its tile's 64.  Positions past
+ *     N rows or nb blocks are zero.
  *
  * Definition computed (the plain reading):
  *     y[m][n] = sum_{k=0}^{K-1} x[m][k] * (q[n][k] - 8) * d[n][k/32]
@@ -87,12 +95,37 @@ static int code_at(const uint8_t *wq, int64_t K, int64_t n, int64_t k)
     return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
 }
 
+/* Tiled layout: quads of 4 blocks along K, and the byte / scale index of
+ * weight (n, k) and block (n, b). */
+static int64_t quads_of(int64_t K) { return (K / 32 + 3) / 4; }
+
+static int64_t tiled_byte_index(int64_t K, int64_t n, int64_t k)
+{
+    const int64_t b = k / 32, g = (k % 32) / 8, j = (k % 8) / 2;
+    const int64_t t = n / 16, c = n % 16, q = b / 4, i = b % 4;
+    return (t * quads_of(K) + q) * 1024 + 16 * (16 * g + c) + 4 * i + j;
+}
+
+static int64_t tiled_scale_index(int64_t K, int64_t n, int64_t b)
+{
+    const int64_t t = n / 16, c = n % 16, q = b / 4, i = b % 4;
+    return (t * quads_of(K) + q) * 64 + 4 * c + i;
+}
+
+static int tiled_code_at(const uint8_t *wq, int64_t K, int64_t n, int64_t k)
+{
+    const uint8_t byte = wq[tiled_byte_index(K, n, k)];
+    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
 /* Dequantized weight (n, k) = (q - 8) * d[n][k/32], exact in fp64. */
 static double weight_at(const uint8_t *wq, const uint16_t *scales,
-                        int64_t K, int64_t n, int64_t k)
+                        int64_t K, int64_t n, int64_t k, int tiled)
 {
-    const int q = code_at(wq, K, n, k);
-    const double d = q4o_f16_to_f64(scales[n * (K / 32) + k / 32]);
+    const int q = tiled ? tiled_code_at(wq, K, n, k) : code_at(wq, K, n, k);
+    const uint16_t dbits = tiled ? scales[tiled_scale_index(K, n, k / 32)]
+                                 : scales[n * (K / 32) + k / 32];
+    const double d = q4o_f16_to_f64(dbits);
     return (double)(q - 8) * d;
 }
 
@@ -115,14 +148,50 @@ void q4o_unpack(const uint8_t *wq, uint8_t *codes, int64_t N, int64_t K)
             codes[n * K + k] = (uint8_t)code_at(wq, K, n, k);
 }
 
+/* Sizes of the tiled layout: code bytes and scale entries. */
+int64_t q4o_tiled_code_bytes(int64_t N, int64_t K) { return (N + 15) / 16 * quads_of(K) * 1024; }
+int64_t q4o_tiled_scale_count(int64_t N, int64_t K) { return (N + 15) / 16 * quads_of(K) * 64; }
+
+/* Pack into the tiled layout: codes u8 [N][K] (low 4 bits used) and scales
+ * fp16 bits [N][K/32] -> tiled codes and tiled scales (padding zeroed). */
+void q4o_pack_tiled(const uint8_t *codes, const uint16_t *scales, uint8_t *wq_t,
+                    uint16_t *sc_t, int64_t N, int64_t K)
+{
+    for (int64_t i = 0; i < q4o_tiled_code_bytes(N, K); ++i)
+        wq_t[i] = 0;
+    for (int64_t i = 0; i < q4o_tiled_scale_count(N, K); ++i)
+        sc_t[i] = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; k += 2) {
+            const uint8_t lo = codes[n * K + k] & 0x0F;
+            const uint8_t hi = codes[n * K + k + 1] & 0x0F;
+            wq_t[tiled_byte_index(K, n, k)] = (uint8_t)(lo | (hi << 4));
+        }
+        for (int64_t b = 0; b < K / 32; ++b)
+            sc_t[tiled_scale_index(K, n, b)] = scales[n * (K / 32) + b];
+    }
+}
+
+/* Inverse of q4o_pack_tiled: -> codes u8 [N][K] in 0..15, scales [N][K/32]. */
+void q4o_unpack_tiled(const uint8_t *wq_t, const uint16_t *sc_t, uint8_t *codes,
+                      uint16_t *scales, int64_t N, int64_t K)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k)
+            codes[n * K + k] = (uint8_t)tiled_code_at(wq_t, K, n, k);
+        for (int64_t b = 0; b < K / 32; ++b)
+            scales[n * (K / 32) + b] = sc_t[tiled_scale_index(K, n, b)];
+    }
+}
+
 /* One output and its normaliser, summing in ascending k. */
 static void one_output(const double *xrow, const uint8_t *wq,
-                       const uint16_t *scales, int64_t K, int64_t n,
+                       const uint16_t *scales, int64_t K, int64_t n, int tiled,
                        double *y_out, double *a_out)
 {
     double acc = 0.0, mag = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        const double t = xrow[k] * weight_at(wq, scales, K, n, k);
+        const double t = xrow[k] * weight_at(wq, scales, K, n, k, tiled);
         acc += t;
         mag += fabs(t);
     }
@@ -142,12 +211,13 @@ static double *decode_x(const uint16_t *x, int x_is_bf16, int64_t M, int64_t K)
 
 /*
  * Full product.  x: u16 bit patterns [M][K] (fp16 if x_is_bf16 == 0, else
- * bf16); wq: u8 [N][K/2]; scales: fp16 bits [N][K/32]; y, a: double [M][N].
- * Returns 0, or -1 if K is not a positive multiple of 32 or memory runs out.
+ * bf16); wq, scales: canonical ([N][K/2], [N][K/32]) if tiled == 0, else the
+ * tiled layout; y, a: double [M][N].  Returns 0, or -1 if K is not a
+ * positive multiple of 32 or memory runs out.
  */
-int q4o_linear(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
-               const uint16_t *scales, int64_t M, int64_t N, int64_t K,
-               double *y, double *a)
+int q4o_linear_fmt(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
+                   const uint16_t *scales, int64_t M, int64_t N, int64_t K,
+                   int tiled, double *y, double *a)
 {
     if (K <= 0 || K % 32 != 0 || M < 0 || N < 0)
         return -1;
@@ -157,19 +227,26 @@ int q4o_linear(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t m = 0; m < M; ++m)
-            one_output(xd + m * K, wq, scales, K, n, &y[m * N + n], &a[m * N + n]);
+            one_output(xd + m * K, wq, scales, K, n, tiled, &y[m * N + n], &a[m * N + n]);
     free(xd);
     return 0;
 }
 
+int q4o_linear(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
+               const uint16_t *scales, int64_t M, int64_t N, int64_t K,
+               double *y, double *a)
+{
+    return q4o_linear_fmt(x, x_is_bf16, wq, scales, M, N, K, 0, y, a);
+}
+
 /*
  * Selected outputs only: for i < count, output (ms[i], ns[i]) goes to y[i]
- * and a[i].  Same arithmetic as q4o_linear, for spot checks of products too
- * large to evaluate whole.
+ * and a[i].  Same arithmetic as q4o_linear_fmt (either layout), for spot
+ * checks of products too large to evaluate whole.
  */
 int q4o_linear_sampled(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
                        const uint16_t *scales, int64_t M, int64_t N, int64_t K,
-                       const int64_t *ms, const int64_t *ns, int64_t count,
+                       int tiled, const int64_t *ms, const int64_t *ns, int64_t count,
                        double *y, double *a)
 {
     if (K <= 0 || K % 32 != 0)
@@ -189,7 +266,7 @@ int q4o_linear_sampled(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
                 continue;
             for (int64_t k = 0; k < K; ++k)
                 xrow[k] = x_value(x[ms[i] * K + k], x_is_bf16);
-            one_output(xrow, wq, scales, K, ns[i], &y[i], &a[i]);
+            one_output(xrow, wq, scales, K, ns[i], tiled, &y[i], &a[i]);
         }
         free(xrow);
     }

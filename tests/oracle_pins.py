@@ -13,7 +13,9 @@ disagrees with what the definition and the mathematics fix:
 * pack       -- numpy nibble packing, and unpack(pack(c)) == c & 15;
 * special    -- closed forms: one-hot input reads out one weight exactly,
                 all codes 8 give 0, zero input gives 0, one block with unit
-                input gives d * sum(q - 8).
+                input gives d * sum(q - 8);
+* tiled      -- the tiled layout against numpy's reshape construction, its
+                round trip, and tiled products equal to canonical ones.
 
 The definition being pinned ("Why Continuous Batching Slowed Down My LLM
 Inference Engine: A Metal Kernel Investigation", section "Two Rows of Input,
@@ -207,6 +209,48 @@ def pin_pack(lib, seed: int = 3) -> None:
         assert np.array_equal(oracle.unpack(wq, K, lib=lib), codes & 0x0F), "unpack (%d,%d)" % (N, K)
 
 
+def np_pack_tiled(codes: np.ndarray, scales: np.ndarray):
+    """The tiled layout built with numpy reshapes: pad to 16 rows and 4-block
+    quads, pack nibbles canonically, then order (tile, quad, g, row, block, j)."""
+    N, K = codes.shape
+    nb = K // 32
+    n16 = -(-N // 16) * 16
+    nb4 = -(-nb // 4) * 4
+    Q = nb4 // 4
+    c = np.zeros((n16, nb4 * 32), np.uint8)
+    c[:N, :K] = np.asarray(codes, np.uint8) & 0x0F
+    byt = (c[:, 0::2] | (c[:, 1::2] << 4)).reshape(n16 // 16, 16, Q, 4, 4, 4)  # t, row, q, i, g, j
+    wq = byt.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+    s = np.zeros((n16, nb4), np.uint16)
+    s[:N, :nb] = scales
+    sc = s.reshape(n16 // 16, 16, Q, 4).transpose(0, 2, 1, 3).reshape(-1)
+    return wq, sc
+
+
+def pin_tiled(lib, seed: int = 6) -> None:
+    """Tiled layout: numpy's construction of the bytes, a round trip, and the
+    product from tiled weights equal (bit for bit) to the canonical one."""
+    rng = np.random.default_rng(seed)
+    for (M, N, K) in ((2, 1, 32), (3, 17, 96), (1, 16, 128), (4, 40, 320), (2, 33, 32 * 13)):
+        codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        s_bits = random_scale_bits(rng, (N, K // 32))
+        wq_t, sc_t = oracle.pack_tiled(codes, s_bits, lib=lib)
+        wq_np, sc_np = np_pack_tiled(codes, s_bits)
+        assert np.array_equal(wq_t, wq_np), "tiled code bytes (%d, %d)" % (N, K)
+        assert np.array_equal(sc_t, sc_np), "tiled scales (%d, %d)" % (N, K)
+        c2, s2 = oracle.unpack_tiled(wq_t, sc_t, N, K, lib=lib)
+        assert np.array_equal(c2, codes & 0x0F) and np.array_equal(s2, s_bits), "tiled round trip"
+        x = rng.normal(0, 1, size=(M, K)).astype(np.float16).view(np.uint16)
+        y_c, a_c = oracle.linear(x, False, np_pack(codes), s_bits, lib=lib)
+        y_t, a_t = oracle.linear_tiled(x, False, wq_t, sc_t, N, K, lib=lib)
+        assert np.array_equal(y_c, y_t) and np.array_equal(a_c, a_t), "tiled product (%d, %d)" % (N, K)
+    # the hand-worked example through the tiled layout
+    g, xv, codes, scales, packed = hand_example_inputs()
+    wq_t, sc_t = oracle.pack_tiled(codes, scales, lib=lib)
+    y, _ = oracle.linear_tiled(xv.astype(np.float16).view(np.uint16), False, wq_t, sc_t, 1, 64, lib=lib)
+    assert np.array_equal(y[:, 0], np.array([float(v) for v in g["y"]])), "hand example, tiled"
+
+
 def pin_special(lib, seed: int = 4) -> None:
     rng = np.random.default_rng(seed)
     N, K = 6, 128
@@ -249,4 +293,5 @@ ALL_PINS = {
     "dense": pin_dense,
     "pack": pin_pack,
     "special": pin_special,
+    "tiled": pin_tiled,
 }

@@ -18,10 +18,16 @@ from tests import oracle_pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "q4_oracle.c")
 
 MUTANTS = {
-    "nibble_order": ("(byte & 0x0F) : (byte >> 4)", "(byte >> 4) : (byte & 0x0F)"),
+    "nibble_order": ("k / 2];\n    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                     "k / 2];\n    return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    "tiled_nibble_order": ("(K, n, k)];\n    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                           "(K, n, k)];\n    return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    "tiled_lane_order": ("16 * (16 * g + c)", "16 * (4 * c + g)"),
+    "tiled_scale_order": ("* 64 + 4 * c + i", "* 64 + 16 * i + c"),
+    "tiled_quad_stride": ("(t * quads_of(K) + q) * 1024", "(q * ((n + 15) / 16 + 1) + t) * 1024"),
     "offset_7": ("(double)(q - 8)", "(double)(q - 7)"),
-    "scale_index": ("scales[n * (K / 32) + k / 32]", "scales[n * (K / 32) + (k / 32 + 1) % (K / 32)]"),
-    "scale_per_16": ("scales[n * (K / 32) + k / 32]", "scales[n * (K / 32) + (k / 16) % (K / 32)]"),
+    "scale_index": (": scales[n * (K / 32) + k / 32]", ": scales[n * (K / 32) + (k / 32 + 1) % (K / 32)]"),
+    "scale_per_16": (": scales[n * (K / 32) + k / 32]", ": scales[n * (K / 32) + (k / 16) % (K / 32)]"),
     "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        const double t",
                           "for (int64_t k = 0; k < K - 1; ++k) {\n        const double t"),
     "flipped_sign": ("acc += t;", "acc -= t;"),
@@ -29,7 +35,9 @@ MUTANTS = {
     "f16_bias": ("expo - 25)", "expo - 24)"),
     "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "bf16_bias": ("expo - 134)", "expo - 133)"),
-    "pack_shift": ("(hi << 4)", "(hi << 3)"),
+    "pack_shift": ("wq[n * (K / 2) + j] = (uint8_t)(lo | (hi << 4));",
+                   "wq[n * (K / 2) + j] = (uint8_t)(lo | (hi << 3));"),
+    "tiled_pack_shift": ("(K, n, k)] = (uint8_t)(lo | (hi << 4));", "(K, n, k)] = (uint8_t)(lo | (hi << 3));"),
     "abs_dropped": ("mag += fabs(t);", "mag += t;"),
 }
 
