@@ -74,18 +74,18 @@ def main() -> int:
     torch.cuda.set_device(dev)
     mats = synth.SET_7B
     Ms = list(range(1, 9))
-    set_bytes = sum(m.N * m.K // 2 + m.N * m.K // 16 for m in mats)
+    set_bytes = sum(sum(q4.packed_sizes(m.N, m.K)) for m in mats)
     P = max(2, int(np.ceil(args.pool_gib * (1 << 30) / set_bytes)))
     log("device %s, rotation pool %d copies of the layer set (%.2f GiB)"
         % (torch.cuda.get_device_name(dev), P, P * set_bytes / (1 << 30)))
 
-    # ---- inputs, resident in HBM
-    base_w, base_s = [], []
+    # ---- inputs, resident in HBM: weights drawn directly in the packed form
+    base = []
     for mi, m in enumerate(mats):
-        base_w.append(torch.from_numpy(synth.packed_codes(m.N, m.K, 3, mi)).to(dev))
-        base_s.append(torch.from_numpy(synth.scales(m.N, m.K, 3, mi).view(np.int16)).to(dev).view(torch.float16))
-    pool = [[(base_w[i].clone(), base_s[i].clone()) for i in range(len(mats))] for _ in range(P)]
-    del base_w, base_s
+        wq_t, sc_t = synth.packed_weight(m.N, m.K, 3, mi)
+        base.append(q4.Q4Weight(torch.from_numpy(wq_t).to(dev),
+                                torch.from_numpy(sc_t.view(np.int16)).to(dev).view(torch.float16), m.N, m.K))
+    pool = [[q4.Q4Weight(b.codes.clone(), b.scales.clone(), b.N, b.K) for b in base] for _ in range(P)]
     Mmax = 128
     xs = {}
     for K in sorted({m.K for m in mats}):
@@ -97,8 +97,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def call(mi, M, p, kernel):
-        w, s = pool[p][mi]
-        q4.linear(xs[mats[mi].K][:M], w, s, out=ys[(mi, M)], kernel=kernel)
+        q4.linear(xs[mats[mi].K][:M], pool[p][mi], out=ys[(mi, M)], kernel=kernel)
 
     def capture(fn):
         # warm the launch path (and any workspace) once outside capture
@@ -183,14 +182,14 @@ def main() -> int:
         oracle.load_library()
         done_bytes, done_rows, t_cpu, sample = 0, 0, 0.0, []
         x_host = {K: xs[K][:8].view(torch.int16).cpu().numpy().view(np.uint16) for K in xs}
-        w_host = [(pool[0][mi][0].cpu().numpy(), pool[0][mi][1].view(torch.int16).cpu().numpy().view(np.uint16))
+        w_host = [(base[mi].codes.cpu().numpy(), base[mi].scales.view(torch.int16).cpu().numpy().view(np.uint16))
                   for mi in range(len(mats))]
         for M in Ms:
             for mi, m in enumerate(mats):
                 if t_cpu > args.cpu_seconds:
                     break
                 t0 = time.perf_counter()
-                oracle.linear(x_host[m.K][:M], True, w_host[mi][0], w_host[mi][1])
+                oracle.linear_tiled(x_host[m.K][:M], True, w_host[mi][0], w_host[mi][1], m.N, m.K)
                 t_cpu += time.perf_counter() - t0
                 done_bytes += synth.algorithmic_bytes(M, m.N, m.K)
                 done_rows += M

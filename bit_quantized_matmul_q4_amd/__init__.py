@@ -1,31 +1,48 @@
 """MI355X-native 4-bit block-quantized linear layer.
 
-    y = linear(x, wq, scales)        # y[M, N] = x[M, K] . dequant(Wq[N, K])^T
+    w = pack(codes, scales)           # canonical -> the library's packed form
+    y = linear(x, w)                  # y[M, N] = x[M, K] . dequant(W[N, K])^T
 
 A thin binding over libq4.so (include/q4.h): every step runs in the HIP
 kernels; this module only checks tensors and passes device pointers and the
 current HIP stream.  PyTorch supplies device memory and streams.
 
 Format: blocks of 32 weights along K with one fp16 scale d each, 4-bit codes
-q in 0..15, weight (q - 8) * d; ``wq`` is uint8 [N, K/2] (low nibble = even
-k), ``scales`` is float16 [N, K/32], ``x`` is bfloat16 or float16 [M, K],
-``y`` is float32 [M, N].
+q in 0..15, weight (q - 8) * d.  Canonical inputs: ``codes`` uint8 [N, K]
+(one code per byte), ``scales`` float16 [N, K/32].  ``pack`` turns them into
+the packed (tiled) form held by a ``Q4Weight``; ``x`` is bfloat16 or float16
+[M, K], ``y`` is float32 [M, N].
 """
 from __future__ import annotations
 
 import ctypes
+from dataclasses import dataclass
 
 import torch
 
 from . import _lib
 from ._lib import KERNELS, Q4Error
 
-__all__ = ["linear", "pack", "workspace_bytes", "get_crossover", "set_crossover",
-           "segments", "Q4Error", "library_path"]
+__all__ = ["Q4Weight", "linear", "pack", "packed_sizes", "workspace_bytes", "get_crossover",
+           "set_crossover", "segments", "Q4Error", "library_path"]
 
 
 def library_path() -> str:
     return _lib.LIB_PATH
+
+
+@dataclass
+class Q4Weight:
+    """A packed N x K weight: ``codes`` uint8 [q4_packed_code_bytes],
+    ``scales`` float16 [q4_packed_scale_bytes / 2], both on one GPU."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    N: int
+    K: int
+
+    @property
+    def device(self) -> torch.device:
+        return self.codes.device
 
 
 def _stream(dev: torch.device):
@@ -41,19 +58,46 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: int, device=None):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
     if t.dtype not in dtypes:
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
-    if t.dim() != ndim:
+    if ndim is not None and t.dim() != ndim:
         raise ValueError("%s must be %d-D, got shape %s" % (name, ndim, tuple(t.shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+def packed_sizes(N: int, K: int):
+    """(packed code bytes, packed scale bytes) of an N x K matrix."""
+    lib = _lib.load()
+    cb, sb = int(lib.q4_packed_code_bytes(N, K)), int(lib.q4_packed_scale_bytes(N, K))
+    if cb == 0:
+        raise ValueError("bad shape N=%d K=%d (K must be a positive multiple of 32)" % (N, K))
+    return cb, sb
+
+
+def pack(codes: torch.Tensor, scales: torch.Tensor) -> Q4Weight:
+    """codes uint8 [N, K] (low 4 bits used), scales float16 [N, K/32] -> Q4Weight."""
+    lib = _lib.load()
+    _need(codes, "codes", (torch.uint8,), 2)
+    dev = codes.device
+    _need(scales, "scales", (torch.float16,), 2, dev)
+    N, K = codes.shape
+    if tuple(scales.shape) != (N, K // 32):
+        raise ValueError("scales must be [%d, %d]" % (N, K // 32))
+    cb, sb = packed_sizes(N, K)
+    wq = torch.empty(cb, dtype=torch.uint8, device=dev)
+    ws = torch.empty(sb // 2, dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.q4_pack(codes.data_ptr(), scales.data_ptr(), wq.data_ptr(), ws.data_ptr(), N, K, _stream(dev))
+    _lib.check(st, "q4_pack")
+    return Q4Weight(wq, ws, N, K)
 
 
 def workspace_bytes(M: int, N: int, K: int, kernel: str = "auto") -> int:
     return int(_lib.load().q4_workspace_bytes(M, N, K, KERNELS[kernel]))
 
 
-def linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, out: torch.Tensor | None = None,
-           kernel: str = "auto", workspace: torch.Tensor | bool | None = True) -> torch.Tensor:
-    """y = x . dequant(wq, scales)^T on the current stream of x's device.
+def linear(x: torch.Tensor, w: Q4Weight, out: torch.Tensor | None = None, kernel: str = "auto",
+           workspace: torch.Tensor | bool | None = True) -> torch.Tensor:
+    """y = x . dequant(w)^T on the current stream of x's device.
 
     kernel: "auto" (crossover rule), "gemv" or "gemm" (forced).  The result
     bits do not depend on this choice.
@@ -64,13 +108,17 @@ def linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, out: torch.T
     lib = _lib.load()
     _need(x, "x", (torch.bfloat16, torch.float16), 2)
     dev = x.device
-    _need(wq, "wq", (torch.uint8,), 2, dev)
-    _need(scales, "scales", (torch.float16,), 2, dev)
+    if not isinstance(w, Q4Weight):
+        raise TypeError("w must be a Q4Weight (see pack)")
+    _need(w.codes, "w.codes", (torch.uint8,), 1, dev)
+    _need(w.scales, "w.scales", (torch.float16,), 1, dev)
     M, K = x.shape
-    N = wq.shape[0]
-    if tuple(wq.shape) != (N, K // 2) or tuple(scales.shape) != (N, K // 32):
-        raise ValueError("shape mismatch: x %s, wq %s, scales %s"
-                         % (tuple(x.shape), tuple(wq.shape), tuple(scales.shape)))
+    N = w.N
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    cb, sb = packed_sizes(N, K)
+    if w.codes.numel() != cb or w.scales.numel() * 2 != sb:
+        raise ValueError("packed weight sizes do not match N=%d K=%d" % (N, K))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
     else:
@@ -90,27 +138,9 @@ def linear(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, out: torch.T
             ws_ptr, ws_len = ws.data_ptr(), need
     dtype = _lib.Q4_BF16 if x.dtype == torch.bfloat16 else _lib.Q4_F16
     with torch.cuda.device(dev):
-        st = lib.q4_linear_ex(x.data_ptr(), dtype, wq.data_ptr(), scales.data_ptr(), out.data_ptr(),
+        st = lib.q4_linear_ex(x.data_ptr(), dtype, w.codes.data_ptr(), w.scales.data_ptr(), out.data_ptr(),
                               M, N, K, KERNELS[kernel], ws_ptr, ws_len, _stream(dev))
     _lib.check(st, "q4_linear_ex")
-    return out
-
-
-def pack(codes: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """codes uint8 [N, K] (low 4 bits used) -> packed uint8 [N, K/2]."""
-    lib = _lib.load()
-    _need(codes, "codes", (torch.uint8,), 2)
-    N, K = codes.shape
-    dev = codes.device
-    if out is None:
-        out = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    else:
-        _need(out, "out", (torch.uint8,), 2, dev)
-        if tuple(out.shape) != (N, K // 2):
-            raise ValueError("out must be [%d, %d]" % (N, K // 2))
-    with torch.cuda.device(dev):
-        st = lib.q4_pack(codes.data_ptr(), out.data_ptr(), N, K, _stream(dev))
-    _lib.check(st, "q4_pack")
     return out
 
 

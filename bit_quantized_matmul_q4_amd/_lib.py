@@ -32,11 +32,12 @@ KERNELS = {"auto": Q4_AUTO, "gemv": Q4_GEMV, "gemm": Q4_GEMM}
 
 EXPORTS = (
     "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_workspace_bytes", "q4_pack",
+    "q4_packed_code_bytes", "q4_packed_scale_bytes",
     "q4_get_crossover", "q4_set_crossover", "q4_segments", "q4_strerror",
     "q4_last_hip_error", "q4_abi_version",
 )
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class Q4Error(RuntimeError):
@@ -63,8 +64,12 @@ def _declare(lib):
     lib.q4_linear_ex.restype = i
     lib.q4_workspace_bytes.argtypes = [i, i, i, i]
     lib.q4_workspace_bytes.restype = sz
-    lib.q4_pack.argtypes = [vp, vp, i, i, vp]
+    lib.q4_pack.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.q4_pack.restype = i
+    lib.q4_packed_code_bytes.argtypes = [i, i]
+    lib.q4_packed_code_bytes.restype = sz
+    lib.q4_packed_scale_bytes.argtypes = [i, i]
+    lib.q4_packed_scale_bytes.restype = sz
     lib.q4_get_crossover.argtypes = []
     lib.q4_get_crossover.restype = i
     lib.q4_set_crossover.argtypes = [i]

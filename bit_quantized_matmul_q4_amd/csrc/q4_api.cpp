@@ -94,7 +94,7 @@ const char *q4_strerror(int status)
     case Q4_OK: return "ok";
     case Q4_ERR_NULL: return "a required pointer is NULL";
     case Q4_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 32, K % 32 == 0, sizes in range)";
-    case Q4_ERR_ALIGN: return "misaligned pointer (x, Wq: 16 B; scales: 2 B; y: 4 B; workspace: 256 B)";
+    case Q4_ERR_ALIGN: return "misaligned pointer (x, Wq: 16 B; packed scales: 8 B; y: 4 B; workspace: 256 B)";
     case Q4_ERR_ENUM: return "unknown dtype or kernel selector";
     case Q4_ERR_HIP: return "HIP launch error (see q4_last_hip_error)";
     case Q4_ERR_WORKSPACE: return "workspace_bytes > 0 with a NULL workspace";
@@ -144,7 +144,7 @@ int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
     const int sh = check_shape(M, N, K);
     if (sh != Q4_OK)
         return sh;
-    if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(scales, 2) || !aligned(y, 4))
+    if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(scales, 8) || !aligned(y, 4))
         return Q4_ERR_ALIGN;
     if (workspace_bytes > 0 && !workspace)
         return Q4_ERR_WORKSPACE;
@@ -176,15 +176,32 @@ int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y, i
     return q4_linear_ex(x, Q4_F16, Wq, scales, y, M, N, K, Q4_AUTO, nullptr, 0, stream);
 }
 
-int q4_pack(const uint8_t *codes, uint8_t *Wq, int N, int K, void *stream)
+size_t q4_packed_code_bytes(int N, int K)
 {
-    if (!codes || !Wq)
+    if (check_shape(1, N, K) != Q4_OK)
+        return 0;
+    return q4::packed_code_bytes(N, K);
+}
+
+size_t q4_packed_scale_bytes(int N, int K)
+{
+    if (check_shape(1, N, K) != Q4_OK)
+        return 0;
+    return q4::packed_scale_bytes(N, K);
+}
+
+int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
+            void *stream)
+{
+    if (!codes || !scales || !Wq || !Wscales)
         return Q4_ERR_NULL;
-    if (N < 1 || K < 32 || K % 32 != 0 || (long long)N * K > (1LL << 46))
-        return Q4_ERR_SHAPE;
-    if (!aligned(Wq, 16))
+    const int sh = check_shape(1, N, K);
+    if (sh != Q4_OK)
+        return sh;
+    if (!aligned(scales, 2) || !aligned(Wq, 16) || !aligned(Wscales, 8))
         return Q4_ERR_ALIGN;
-    return hip_status(q4::launch_pack(codes, Wq, N, K, (hipStream_t)stream));
+    return hip_status(q4::launch_pack(codes, (const uint16_t *)scales, Wq, (uint16_t *)Wscales, N, K,
+                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

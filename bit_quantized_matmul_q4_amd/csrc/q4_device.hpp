@@ -21,6 +21,15 @@
 //   tree:     for h = 1, 2, 4, .. S/2: p_j = p_j + p_{j+h} for j % 2h == 0.
 //   output:   y[m][n] = 16 * p_0   (exact: undoes the 1/16 of the operand).
 // S depends on K only, so slicing N (sharding) keeps every bit.
+//
+// Weight layout read by the kernels (written by q4_pack): tiles of 16
+// columns (t = n / 16, c = n % 16) by one quad (q = b / 4, i = b % 4),
+// ordered [ceil(N/16)][G].  A tile holds 1024 code bytes, 16 per lane of a
+// wave in lane order l = 16 g + c: bytes 4 i .. 4 i + 3 of lane l are bytes
+// 4 g .. 4 g + 3 of block 4 q + i of column n in the row-major packing
+// (codes of k = 32 b + 8 g .. + 7, low nibble first).  So one 16-byte load
+// gives lane (g, c) exactly the B-operand dwords of the tile's four block
+// dots.  Then 64 fp16 scales, [c][i].  Padding (n >= N, b >= nb) is zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,34 +47,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- dequant
-// v_cvt_off_f32_i4 reads bits 3..0 of its (SDWA-selected) source as a signed
-// 4-bit integer t and returns t / 16.  With t = q ^ 8, t is q - 8 in two's
-// complement, so each call yields (q - 8) / 16 exactly.
-__device__ __forceinline__ float i4_b0(uint32_t v) { return __builtin_amdgcn_cvt_off_f32_i4((int)v); }
-
-__device__ __forceinline__ float i4_b1(uint32_t v)
-{
-    float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
-        : "=v"(r) : "v"(v));
-    return r;
-}
-
-__device__ __forceinline__ float i4_b2(uint32_t v)
-{
-    float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
-        : "=v"(r) : "v"(v));
-    return r;
-}
-
-__device__ __forceinline__ float i4_b3(uint32_t v)
-{
-    float r;
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
-        : "=v"(r) : "v"(v));
-    return r;
-}
+// v_cvt_off_f32_i4 reads bits 3..0 of its source as a signed 4-bit integer
+// t and returns t / 16.  With t = q ^ 8, t is q - 8 in two's complement, so
+// each call yields (q - 8) / 16 exactly.  Only the compiler builtin is used
+// (no inline assembly): the compiler then tracks every register the
+// conversions write against in-flight matrix-core instructions.
+__device__ __forceinline__ float i4_at(uint32_t v) { return __builtin_amdgcn_cvt_off_f32_i4((int)v); }
 
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi)
@@ -84,12 +71,12 @@ template <bool BF16>
 __device__ __forceinline__ u32x4 dequant8(uint32_t w)
 {
     const uint32_t t = w ^ 0x88888888u;
-    const uint32_t h = t >> 4;
+    const uint32_t h = (w >> 4) ^ 0x08888888u;
     u32x4 r;
-    r.x = pack2<BF16>(i4_b0(t), i4_b0(h));
-    r.y = pack2<BF16>(i4_b1(t), i4_b1(h));
-    r.z = pack2<BF16>(i4_b2(t), i4_b2(h));
-    r.w = pack2<BF16>(i4_b3(t), i4_b3(h));
+    r.x = pack2<BF16>(i4_at(t), i4_at(h));
+    r.y = pack2<BF16>(i4_at(t >> 8), i4_at(h >> 8));
+    r.z = pack2<BF16>(i4_at(t >> 16), i4_at(h >> 16));
+    r.w = pack2<BF16>(i4_at(t >> 24), i4_at(h >> 24));
     return r;
 }
 
@@ -121,6 +108,35 @@ __device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 s)
     p.y = __builtin_fmaf(d, s.y, p.y);
     p.z = __builtin_fmaf(d, s.z, p.z);
     p.w = __builtin_fmaf(d, s.w, p.w);
+}
+
+// Streaming form of the pairwise tree for one wave that owns an aligned run
+// of L segments (L a power of two, at most 2^LV): call after each finished
+// segment li = 0..L-1 with its partial in cur.  Left subtrees wait in stack
+// (a binary counter over li); after li = L-1, cur holds the run's subtree
+// root and the call returns true.  Otherwise cur must restart from +0.
+template <int LV, int NACC>
+__device__ __forceinline__ bool tree_push(f32x4 (&stack)[LV][NACC], f32x4 (&cur)[NACC], int li, int L)
+{
+    int lvl = 0;
+#pragma unroll
+    for (int l = 0; l < LV; ++l) {
+        if (lvl == l && ((li >> l) & 1)) {
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                cur[a] = stack[l][a] + cur[a];
+            lvl = l + 1;
+        }
+    }
+    if ((1 << lvl) >= L)
+        return true;
+#pragma unroll
+    for (int l = 0; l < LV; ++l)
+        if (l == lvl)
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                stack[l][a] = cur[a];
+    return false;
 }
 
 // Pairwise tree over v[0..S): the fixed order of the contract.

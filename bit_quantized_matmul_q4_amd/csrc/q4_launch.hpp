@@ -21,6 +21,12 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
 // Bytes of workspace the matrix-matrix kernel can use for this shape.
 size_t gemm_workspace_bytes(int M, int N, int K);
 
-hipError_t launch_pack(const uint8_t *codes, uint8_t *wq, int N, int K, hipStream_t stream);
+// Canonical codes [N][K] and scales [N][K/32] -> the tiled layout.
+hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales_in, uint8_t *wq, uint16_t *scales_out,
+                       int N, int K, hipStream_t stream);
+
+// Sizes of the tiled layout.
+size_t packed_code_bytes(int N, int K);
+size_t packed_scale_bytes(int N, int K);
 
 }  // namespace q4

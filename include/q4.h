@@ -17,11 +17,21 @@
  *
  * Weight format (the pages say only "4-bit quantized"; the library fixes):
  *   - blocks of 32 consecutive weights along K; one IEEE binary16 scale d
- *     per block; 4-bit codes q in 0..15; weight value (q - 8) * d;
- *   - Wq: uint8 [N][K/2], row-major; byte j of row n holds the code of
- *     k = 2j in bits 0..3 and of k = 2j+1 in bits 4..7;
- *   - scales: binary16 [N][K/32], row-major (zero and subnormal scales are
- *     legal and used exactly; inf/nan scales are outside the contract).
+ *     per block; 4-bit codes q in 0..15; weight value (q - 8) * d (zero and
+ *     subnormal scales are legal and used exactly; inf/nan scales are
+ *     outside the contract);
+ *   - canonical form (input of q4_pack): codes uint8 [N][K] (one code per
+ *     byte, bits 0..3), scales binary16 [N][K/32], both row-major;
+ *   - packed form (what q4_pack writes and the compute calls read): tiles
+ *     of 16 rows (t = n / 16, c = n % 16) by 4 blocks (quad q = b / 4,
+ *     i = b % 4), tile order [ceil(N/16)][ceil(K/128)].
+ *       Wq: 1024 bytes per tile.  With g, j in 0..3, the byte at
+ *         16 * (16 g + c) + 4 i + j holds the codes of k = 32 b + 8 g + 2 j
+ *         (bits 0..3) and k + 1 (bits 4..7) of row n, block b = 4 q + i.
+ *       Wscales: 64 binary16 per tile; element 4 c + i is d[n][b].
+ *     Entries past N rows or K/32 blocks are zero.  The layout makes each
+ *     16-byte load of a 64-lane wave contiguous and gives every lane the
+ *     exact matrix-core operand words it needs.
  * Activations x: [M][K] row-major, bfloat16 (q4_linear) or binary16
  * (q4_linear_f16).  Output y: float32 [M][N] row-major, overwritten (no
  * bias, no accumulation into y).
@@ -47,14 +57,14 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 enum q4_status {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,      /* a required pointer is NULL */
     Q4_ERR_SHAPE = -2,     /* M < 1, N < 1, K < 32, K % 32 != 0, or a size overflows */
-    Q4_ERR_ALIGN = -3,     /* x or Wq not 16-byte aligned, scales not 2-byte aligned,
-                              y not 4-byte aligned */
+    Q4_ERR_ALIGN = -3,     /* x or Wq not 16-byte aligned, packed scales not 8-byte
+                              aligned, y not 4-byte aligned (see each call) */
     Q4_ERR_ENUM = -4,      /* unknown dtype or kernel selector */
     Q4_ERR_HIP = -5,       /* a HIP call failed (see q4_last_hip_error) */
     Q4_ERR_WORKSPACE = -6  /* workspace_bytes non-zero with a NULL workspace */
@@ -70,10 +80,10 @@ enum q4_kernel {
 
 /*
  * y = x . dequant(Wq)^T with bfloat16 activations.
- *   x      bf16  [M][K]      device, 16-byte aligned
- *   Wq     uint8 [N][K/2]    device, 16-byte aligned
- *   scales fp16  [N][K/32]   device, 2-byte aligned
- *   y      fp32  [M][N]      device, 4-byte aligned, overwritten
+ *   x      bf16  [M][K]          device, 16-byte aligned
+ *   Wq     packed codes          device, 16-byte aligned, q4_packed_code_bytes(N, K)
+ *   scales packed scales         device, 8-byte aligned, q4_packed_scale_bytes(N, K)
+ *   y      fp32  [M][N]          device, 4-byte aligned, overwritten
  * Kernel chosen by the crossover rule (Q4_AUTO), with no workspace.
  */
 int q4_linear(const void *x, const void *Wq, const void *scales, float *y,
@@ -101,12 +111,20 @@ int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
 size_t q4_workspace_bytes(int M, int N, int K, int kernel);
 
 /*
- * Pack 4-bit codes: codes uint8 [N][K] (only bits 0..3 of each byte are
- * used) -> Wq uint8 [N][K/2] with the nibble order above.  Device pointers;
- * codes any alignment, Wq 16-byte aligned; K must be a positive multiple of
- * 32.  Bit-exact; scales are not touched (they pass through unchanged).
+ * Pack the canonical form into the packed form (both described above).
+ *   codes    uint8 [N][K]     device, any alignment; only bits 0..3 used
+ *   scales   fp16 [N][K/32]   device, 2-byte aligned
+ *   Wq       packed codes     device, 16-byte aligned, q4_packed_code_bytes(N, K)
+ *   Wscales  packed scales    device, 8-byte aligned, q4_packed_scale_bytes(N, K)
+ * K must be a positive multiple of 32.  Bit-exact; padding is written as 0.
  */
-int q4_pack(const uint8_t *codes, uint8_t *Wq, int N, int K, void *stream);
+int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
+            void *stream);
+
+/* Bytes of the packed codes and packed scales of an N x K matrix (0 for a
+ * bad shape).  Pure host computation. */
+size_t q4_packed_code_bytes(int N, int K);
+size_t q4_packed_scale_bytes(int N, int K);
 
 /* Crossover threshold T: Q4_AUTO uses the matrix-vector kernel iff M <= T.
  * Initialised from the environment variable Q4_CROSSOVER if set, else the

@@ -93,11 +93,20 @@ def codes(N: int, K: int, workload: int = 0, matrix: int = 0) -> np.ndarray:
     return generator(workload, matrix, T_CODES).integers(0, 16, size=(N, K), dtype=np.uint8)
 
 
-def packed_codes(N: int, K: int, workload: int = 0, matrix: int = 0) -> np.ndarray:
-    """uint8 [N, K/2] of i.i.d. uniform bytes: the packed form of i.i.d.
-    uniform codes (two independent uniform nibbles per byte).  Used where the
-    unpacked codes are never needed, e.g. benchmark weight pools."""
-    return generator(workload, matrix, T_CODES).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+def packed_weight(N: int, K: int, workload: int = 0, matrix: int = 0, sigma: float = 0.02):
+    """A weight already in the library's packed (tiled) form, drawn directly:
+    code bytes are i.i.d. uniform (two independent uniform nibbles per byte,
+    the packed form of i.i.d. uniform codes) and scales |N(0, sigma)| in
+    fp16, over the whole tiled extent (16-row by 4-block tiles).  Padding
+    positions, if the shape has any, hold random values too: the kernels never
+    use them.  For benchmark pools and very large matrices, where the
+    canonical codes are never needed."""
+    tiles = -(-N // 16) * -(-(K // 32) // 4)
+    g = generator(workload, matrix, T_CODES)
+    wq = g.integers(0, 256, size=tiles * 1024, dtype=np.uint8)
+    gs = generator(workload, matrix, T_SCALES)
+    sc = f64_to_f16_bits(np.abs(gs.normal(0.0, sigma, size=tiles * 64)))
+    return wq, sc
 
 
 def scales(N: int, K: int, workload: int = 0, matrix: int = 0, sigma: float = 0.02) -> np.ndarray:

@@ -56,9 +56,19 @@ def y_bits(y: torch.Tensor) -> np.ndarray:
     return y.detach().cpu().numpy().view(np.uint32)
 
 
-def run_linear(x_bits, bf16, wq, s_bits, kernel="auto", workspace=True) -> torch.Tensor:
-    out = q4.linear(x_to_dev(x_bits, bf16), u8_to_dev(wq), scales_to_dev(s_bits), kernel=kernel,
-                    workspace=workspace)
+def pack_dev(codes: np.ndarray, s_bits: np.ndarray) -> "q4.Q4Weight":
+    """Canonical codes [N, K] and scale bits [N, K/32] -> packed on the GPU."""
+    return q4.pack(u8_to_dev(codes), scales_to_dev(s_bits))
+
+
+def weight_from_tiled(wq_t: np.ndarray, sc_t: np.ndarray, N: int, K: int) -> "q4.Q4Weight":
+    """Packed (tiled) bytes built on the host -> a Q4Weight on the GPU."""
+    return q4.Q4Weight(u8_to_dev(wq_t.reshape(-1)), scales_to_dev(sc_t.reshape(-1)), N, K)
+
+
+def run_linear(x_bits, bf16, codes, s_bits, kernel="auto", workspace=True) -> torch.Tensor:
+    """Canonical inputs -> GPU pack -> GPU linear (synchronized)."""
+    out = q4.linear(x_to_dev(x_bits, bf16), pack_dev(codes, s_bits), kernel=kernel, workspace=workspace)
     torch.cuda.synchronize()
     return out
 

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_and_strerror(lib):
-    assert lib.q4_abi_version() == 1
+    assert lib.q4_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
     assert lib.q4_strerror(-99) == b"unknown status"
@@ -71,6 +71,19 @@ def test_segments(lib, K):
 def test_segments_bad_k(lib):
     for K in (0, 16, 31, 33, -32):
         assert lib.q4_segments(K) == 0
+
+
+def test_packed_sizes(lib):
+    """Tiles of 16 rows by 4 blocks: 1024 code bytes and 128 scale bytes each."""
+    import oracle
+    for N, K in ((1, 32), (16, 128), (17, 160), (896, 896), (3584, 18944), (152064, 3584)):
+        tiles = -(-N // 16) * -(-(K // 32) // 4)
+        assert lib.q4_packed_code_bytes(N, K) == 1024 * tiles
+        assert lib.q4_packed_scale_bytes(N, K) == 128 * tiles
+        if N * K < 1 << 24:
+            assert oracle.tiled_sizes(N, K) == (1024 * tiles, 64 * tiles)
+    assert lib.q4_packed_code_bytes(4, 48) == 0
+    assert lib.q4_packed_scale_bytes(0, 64) == 0
 
 
 def test_crossover_get_set(lib):
@@ -122,7 +135,11 @@ def test_argument_checks(lib):
     # the short forms run the same checks
     assert lib.q4_linear(None, FAKE, FAKE, FAKE, 1, 16, 64, None) == _lib.Q4_ERR_NULL
     assert lib.q4_linear_f16(FAKE, FAKE, FAKE, FAKE, 1, 16, 40, None) == _lib.Q4_ERR_SHAPE
-    assert lib.q4_pack(None, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
-    assert lib.q4_pack(FAKE, FAKE, 4, 40, None) == _lib.Q4_ERR_SHAPE
-    assert lib.q4_pack(FAKE, FAKE + 4, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert lib.q4_pack(None, FAKE, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert lib.q4_pack(FAKE, None, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert lib.q4_pack(FAKE, FAKE, FAKE, FAKE, 4, 40, None) == _lib.Q4_ERR_SHAPE
+    assert lib.q4_pack(FAKE, FAKE, FAKE + 4, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert lib.q4_pack(FAKE, FAKE, FAKE, FAKE + 4, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert lib.q4_pack(FAKE, FAKE + 1, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert call(lib, s=FAKE + 4) == _lib.Q4_ERR_ALIGN
     assert lib.q4_last_hip_error() == 0

@@ -15,14 +15,15 @@ pytestmark = pytest.mark.gpu
 SAMPLES = 1500
 
 
-def sampled_check(x_bits, wq, s_bits, y, rng, bf16=True):
+def sampled_check(x_bits, wq_t, sc_t, K, y, rng, bf16=True):
+    """wq_t, sc_t: the packed (tiled) weight as host arrays."""
     M, N = y.shape
     ms = rng.integers(0, M, SAMPLES)
     ns = rng.integers(0, N, SAMPLES)
     # always include the corners (tails of both dimensions)
     ms = np.concatenate([ms, [0, M - 1, 0, M - 1]])
     ns = np.concatenate([ns, [0, 0, N - 1, N - 1]])
-    y_ref, a_ref = oracle.linear_sampled(x_bits, bf16, wq, s_bits, ms, ns)
+    y_ref, a_ref = oracle.linear_sampled(x_bits, bf16, wq_t, sc_t, ms, ns, tiled_nk=(N, K))
     err = oracle.max_normalised_error(y[ms, ns], y_ref, a_ref)
     assert err <= gu.TOL, err
 
@@ -37,33 +38,37 @@ def test_7b_layer_set(mi):
     mat = synth.SET_7B[mi]
     rng = np.random.default_rng(40 + mi)
     x, codes, s = synth.problem(mat.N, mat.K, 124, "bf16", workload=3, matrix=mi)
-    wq = oracle.pack(codes)
-    xd, wd, sd = gu.x_to_dev(x, True), gu.u8_to_dev(wq), gu.scales_to_dev(s)
+    xd, w = gu.x_to_dev(x, True), gu.pack_dev(codes, s)
+    wq_t = w.codes.cpu().numpy()
+    sc_t = w.scales.view(torch.int16).cpu().numpy().view(np.uint16)
     gu.note("7B %s M=8 gemv" % mat.name)
-    y8 = q4.linear(xd[:8], wd, sd, kernel="gemv")
+    y8 = q4.linear(xd[:8], w, kernel="gemv")
     torch.cuda.synchronize()
     y8h = y8.cpu().numpy()
-    sampled_check(x[:8], wq, s, y8h, rng)
+    sampled_check(x[:8], wq_t, sc_t, mat.K, y8h, rng)
+    # the packed bytes the GPU made are the oracle's packing of the same codes
+    # (checked on a row slice to keep the host work small)
+    wq_o, sc_o = oracle.pack_tiled(codes[:64], s[:64])
+    assert np.array_equal(wq_t[:wq_o.size], wq_o) and np.array_equal(sc_t[:sc_o.size], sc_o)
     for M in (1, 3, 8, 16, 124):
         for kernel in ("auto", "gemv", "gemm"):
             gu.note("7B %s M=%d %s" % (mat.name, M, kernel))
-            y = q4.linear(xd[:M], wd, sd, kernel=kernel).cpu().numpy()
+            y = q4.linear(xd[:M], w, kernel=kernel).cpu().numpy()
             assert np.array_equal(y[: min(M, 8)].view(np.uint32), y8h[: min(M, 8)].view(np.uint32))
             if M == 124:
-                sampled_check(x[:124], wq, s, y, rng)
+                sampled_check(x[:124], wq_t, sc_t, mat.K, y, rng)
 
 
 def test_lm_head_sampled():
     mat = synth.LM_HEAD_7B
     rng = np.random.default_rng(50)
     x = synth.activations(64, mat.K, "bf16", workload=5, matrix=6)
-    wq = synth.packed_codes(mat.N, mat.K, workload=5, matrix=6)
-    s = synth.scales(mat.N, mat.K, workload=5, matrix=6)
-    xd, wd, sd = gu.x_to_dev(x, True), gu.u8_to_dev(wq), gu.scales_to_dev(s)
+    wq_t, sc_t = synth.packed_weight(mat.N, mat.K, workload=5, matrix=6)
+    xd, w = gu.x_to_dev(x, True), gu.weight_from_tiled(wq_t, sc_t, mat.N, mat.K)
     ys = {}
     for M in (1, 4, 16, 64):
         gu.note("lm_head M=%d" % M)
-        ys[M] = q4.linear(xd[:M], wd, sd).cpu().numpy()
-        sampled_check(x[:M], wq, s, ys[M], rng)
+        ys[M] = q4.linear(xd[:M], w).cpu().numpy()
+        sampled_check(x[:M], wq_t, sc_t, mat.K, ys[M], rng)
     for M in (1, 4, 16):
         assert np.array_equal(ys[64][:M].view(np.uint32), ys[M].view(np.uint32))

@@ -26,17 +26,16 @@ N = 160
 def prob():
     gu.require_gpu()
     x, codes, s = synth.problem(N, K, 128, "bf16", workload=93, matrix=0)
-    wq = oracle.pack(codes)
-    xd, wd, sd = gu.x_to_dev(x, True), gu.u8_to_dev(wq), gu.scales_to_dev(s)
+    xd, w = gu.x_to_dev(x, True), gu.pack_dev(codes, s)
     rows = []
     for m in range(128):
-        rows.append(q4.linear(xd[m:m + 1].contiguous(), wd, sd, kernel="gemv"))
+        rows.append(q4.linear(xd[m:m + 1].contiguous(), w, kernel="gemv"))
     torch.cuda.synchronize()
     ref = torch.cat(rows).cpu().numpy().view(np.uint32)
-    y_or, a_or = oracle.linear(x, True, wq, s)
+    y_or, a_or = oracle.linear(x, True, oracle.pack(codes), s)
     err = oracle.max_normalised_error(ref.view(np.float32), y_or, a_or)
     assert err <= gu.TOL
-    return x, xd, wd, sd, ref
+    return x, xd, w, codes, s, ref
 
 
 MS = list(range(1, 18)) + [31, 32, 33, 64, 100, 124, 128]
@@ -44,43 +43,43 @@ MS = list(range(1, 18)) + [31, 32, 33, 64, 100, 124, 128]
 
 @pytest.mark.parametrize("kernel", ["gemv", "gemm", "auto"])
 def test_rows_independent_of_m(prob, kernel):
-    x, xd, wd, sd, ref = prob
+    x, xd, w, codes, s, ref = prob
     for M in MS:
         gu.note("invariance over M=%d kernel=%s" % (M, kernel))
-        y = q4.linear(xd[:M], wd, sd, kernel=kernel)
+        y = q4.linear(xd[:M], w, kernel=kernel)
         assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:M]), (M, kernel)
 
 
 def test_workspace_split_same_bits(prob):
-    x, xd, wd, sd, ref = prob
+    x, xd, w, codes, s, ref = prob
     for M in (9, 64, 124):
         gu.note("workspace split M=%d" % M)
-        a = q4.linear(xd[:M], wd, sd, kernel="gemm", workspace=True)
-        b = q4.linear(xd[:M], wd, sd, kernel="gemm", workspace=None)
+        a = q4.linear(xd[:M], w, kernel="gemm", workspace=True)
+        b = q4.linear(xd[:M], w, kernel="gemm", workspace=None)
         assert np.array_equal(a.cpu().numpy().view(np.uint32), ref[:M])
         assert np.array_equal(b.cpu().numpy().view(np.uint32), ref[:M])
 
 
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 def test_permutation_and_companions(prob, kernel):
-    x, xd, wd, sd, ref = prob
+    x, xd, w, codes, s, ref = prob
     rng = np.random.default_rng(31)
     gu.note("permutation kernel=%s" % kernel)
     perm = rng.permutation(128)
-    y = q4.linear(xd[torch.from_numpy(perm).to(gu.DEV)].contiguous(), wd, sd, kernel=kernel)
+    y = q4.linear(xd[torch.from_numpy(perm).to(gu.DEV)].contiguous(), w, kernel=kernel)
     assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[perm])
     gu.note("companion rows kernel=%s" % kernel)
     other = synth.f64_to_bf16_bits(rng.normal(0, 30, size=(40, K)))
     xm = np.concatenate([other[:17], x[5:6], other[17:]])
-    y = q4.linear(gu.x_to_dev(xm, True), wd, sd, kernel=kernel)
+    y = q4.linear(gu.x_to_dev(xm, True), w, kernel=kernel)
     assert np.array_equal(y.cpu().numpy().view(np.uint32)[17], ref[5])
 
 
 def test_repeat_runs_identical(prob):
-    x, xd, wd, sd, ref = prob
+    x, xd, w, codes, s, ref = prob
     for kernel in ("gemv", "gemm"):
         gu.note("repeat kernel=%s" % kernel)
-        outs = [q4.linear(xd[:37], wd, sd, kernel=kernel).cpu().numpy().view(np.uint32) for _ in range(4)]
+        outs = [q4.linear(xd[:37], w, kernel=kernel).cpu().numpy().view(np.uint32) for _ in range(4)]
         for o in outs:
             assert np.array_equal(o, ref[:37])
 
@@ -88,21 +87,29 @@ def test_repeat_runs_identical(prob):
 def test_mixed_124_rows(prob):
     """120 prefill + 4 verify rows: each verify row equals its M=4 and M=1
     results, whichever kernel ran the 124-row batch."""
-    x, xd, wd, sd, ref = prob
+    x, xd, w, codes, s, ref = prob
     for kernel in ("auto", "gemv", "gemm"):
         gu.note("mixed 124 kernel=%s" % kernel)
-        y124 = q4.linear(xd[:124], wd, sd, kernel=kernel).cpu().numpy().view(np.uint32)
-        y4 = q4.linear(xd[120:124].contiguous(), wd, sd, kernel="auto").cpu().numpy().view(np.uint32)
+        y124 = q4.linear(xd[:124], w, kernel=kernel).cpu().numpy().view(np.uint32)
+        y4 = q4.linear(xd[120:124].contiguous(), w, kernel="auto").cpu().numpy().view(np.uint32)
         assert np.array_equal(y124[120:124], y4)
         assert np.array_equal(y124, ref[:124])
 
 
 def test_n_sharding(prob):
-    """Column slices of Wq give the column slices of y, bit for bit (the
-    segment count depends on K only)."""
-    x, xd, wd, sd, ref = prob
+    """Row slices of W give the column slices of y, bit for bit (the segment
+    count depends on K only): slices packed on their own, and tile-aligned
+    slices cut straight out of the packed weight."""
+    x, xd, w, codes, s, ref = prob
     for (n0, n1) in ((0, 16), (16, 80), (80, 160), (37, 121)):
         for kernel in ("gemv", "gemm"):
             gu.note("shard %d:%d kernel=%s" % (n0, n1, kernel))
-            y = q4.linear(xd[:20], wd[n0:n1].contiguous(), sd[n0:n1].contiguous(), kernel=kernel)
+            ws = gu.pack_dev(np.ascontiguousarray(codes[n0:n1]), np.ascontiguousarray(s[n0:n1]))
+            y = q4.linear(xd[:20], ws, kernel=kernel)
             assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:20, n0:n1])
+    G = (K // 32 + 3) // 4
+    for (t0, t1) in ((0, 1), (1, 5), (5, 10)):
+        sl = q4.Q4Weight(w.codes[t0 * G * 1024:t1 * G * 1024], w.scales[t0 * G * 64:t1 * G * 64],
+                         16 * (t1 - t0), K)
+        y = q4.linear(xd[:20], sl, kernel="gemv")
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:20, 16 * t0:16 * t1])

@@ -7,6 +7,7 @@ read-out, the exact regime, the hand-worked example)."""
 import numpy as np
 import pytest
 
+import bit_quantized_matmul_q4_amd as q4
 import oracle
 import synth
 from tests import gpu_util as gu
@@ -21,9 +22,8 @@ def gpu():
 
 
 def check(x_bits, bf16, codes, s_bits, kernel, tol=gu.TOL):
-    wq = oracle.pack(codes)
-    y = gu.run_linear(x_bits, bf16, wq, s_bits, kernel=kernel).cpu().numpy()
-    y_ref, a_ref = oracle.linear(x_bits, bf16, wq, s_bits)
+    y = gu.run_linear(x_bits, bf16, codes, s_bits, kernel=kernel).cpu().numpy()
+    y_ref, a_ref = oracle.linear(x_bits, bf16, oracle.pack(codes), s_bits)
     err = oracle.max_normalised_error(y, y_ref, a_ref)
     assert err <= tol, "normalised error %.3g > %.3g" % (err, tol)
     return y, y_ref, a_ref
@@ -39,7 +39,7 @@ def test_hand_example_exact(kernel):
     y_exp = np.array([float(v) for v in g["y"]], np.float32)
     for bf16 in (True, False):
         xb = synth.f64_to_bf16_bits(xv) if bf16 else synth.f64_to_f16_bits(xv)
-        y = gu.run_linear(xb, bf16, packed, scales, kernel=kernel).cpu().numpy()
+        y = gu.run_linear(xb, bf16, codes, scales, kernel=kernel).cpu().numpy()
         assert np.array_equal(y[:, 0], y_exp), (kernel, bf16, y[:, 0])
 
 
@@ -72,9 +72,8 @@ def test_one_hot_readout_exact(kernel, bf16):
     s = oracle_pins.random_scale_bits(rng, (N, K // 32))
     x = np.zeros((K, K), np.uint16)
     x[np.arange(K), np.arange(K)] = 0x3F80 if bf16 else 0x3C00
-    wq = oracle.pack(codes)
-    y = gu.run_linear(x, bf16, wq, s, kernel=kernel).cpu().numpy()
-    y_ref, _ = oracle.linear(x, bf16, wq, s)
+    y = gu.run_linear(x, bf16, codes, s, kernel=kernel).cpu().numpy()
+    y_ref, _ = oracle.linear(x, bf16, oracle.pack(codes), s)
     assert np.array_equal(y, y_ref.astype(np.float32))
 
 
@@ -89,9 +88,8 @@ def test_exact_regime(kernel, K):
     x = synth.f64_to_bf16_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float64))
     codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
     s = synth.f64_to_f16_bits(2.0 ** -rng.integers(1, 5, size=(N, K // 32)))
-    wq = oracle.pack(codes)
-    y = gu.run_linear(x, True, wq, s, kernel=kernel).cpu().numpy()
-    y_ref, _ = oracle.linear(x, True, wq, s)
+    y = gu.run_linear(x, True, codes, s, kernel=kernel).cpu().numpy()
+    y_ref, _ = oracle.linear(x, True, oracle.pack(codes), s)
     assert np.array_equal(y, y_ref.astype(np.float32))
 
 
@@ -103,15 +101,16 @@ def test_special_cases(kernel):
     x = synth.activations(M, K, "bf16", workload=92)
     s = synth.scales(N, K, workload=92)
     # all codes 8 -> zeros
-    y = gu.run_linear(x, True, oracle.pack(np.full((N, K), 8, np.uint8)), s, kernel=kernel)
+    y = gu.run_linear(x, True, np.full((N, K), 8, np.uint8), s, kernel=kernel)
     assert (y == 0).all()
     # zero input -> zeros
     codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
-    y = gu.run_linear(np.zeros((M, K), np.uint16), True, oracle.pack(codes), s, kernel=kernel)
+    y = gu.run_linear(np.zeros((M, K), np.uint16), True, codes, s, kernel=kernel)
     assert (y == 0).all()
     # single block: y = fl(d * s) with s exact
     xk = synth.f64_to_bf16_bits(rng.integers(-3, 4, size=(M, 32)).astype(np.float64))
-    y = gu.run_linear(xk, True, oracle.pack(codes[:, :32]), s[:, :1], kernel=kernel).cpu().numpy()
+    y = gu.run_linear(xk, True, np.ascontiguousarray(codes[:, :32]), np.ascontiguousarray(s[:, :1]),
+                      kernel=kernel).cpu().numpy()
     y_ref, _ = oracle.linear(xk, True, oracle.pack(codes[:, :32]), s[:, :1])
     assert np.array_equal(y, y_ref.astype(np.float32))
     # subnormal and zero scales, random bit-pattern activations
@@ -128,11 +127,11 @@ def test_small_workloads_full(workload):
     for mi, mat in enumerate(spec["matrices"]):
         Mmax = max(spec["Ms"])
         x, codes, s = synth.problem(mat.N, mat.K, Mmax, spec["x"], workload, mi)
-        wq = oracle.pack(codes)
-        y_ref, a_ref = oracle.linear(x, bf16, wq, s)
+        y_ref, a_ref = oracle.linear(x, bf16, oracle.pack(codes), s)
+        w = gu.pack_dev(codes, s)
         for M in spec["Ms"]:
             for kernel in ("auto", "gemv", "gemm"):
                 gu.note("workload %d %s M=%d kernel=%s" % (workload, mat.name, M, kernel))
-                y = gu.run_linear(x[:M], bf16, wq, s, kernel=kernel).cpu().numpy()
+                y = q4.linear(gu.x_to_dev(x[:M], bf16), w, kernel=kernel).cpu().numpy()
                 err = oracle.max_normalised_error(y, y_ref[:M], a_ref[:M])
                 assert err <= gu.TOL, (mat.name, M, kernel, err)

@@ -1,4 +1,5 @@
-"""q4_pack on the GPU against the oracle's packing: bit-exact."""
+"""q4_pack on the GPU against the oracle's packing into the tiled layout:
+bit-exact codes and scales, padding included."""
 import numpy as np
 import pytest
 import torch
@@ -7,6 +8,7 @@ import bit_quantized_matmul_q4_amd as q4
 import oracle
 import synth
 from tests import gpu_util as gu
+from tests import oracle_pins
 
 pytestmark = pytest.mark.gpu
 
@@ -16,16 +18,20 @@ def gpu():
     gu.require_gpu()
 
 
-SHAPES = [(1, 32), (3, 64), (17, 96), (896, 896), (128, 896), (4864, 896), (896, 4864),
-          (512, 3584), (5, 18944), (33, 32 * 37)]
+SHAPES = [(1, 32), (3, 64), (17, 96), (16, 128), (896, 896), (128, 896), (4864, 896), (896, 4864),
+          (512, 3584), (5, 18944), (33, 32 * 37), (40, 32 * 13)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_pack_matches_oracle(N, K):
     gu.note("pack N=%d K=%d" % (N, K))
     codes = synth.codes(N, K, workload=90, matrix=N)
-    got = q4.pack(gu.u8_to_dev(codes)).cpu().numpy()
-    assert np.array_equal(got, oracle.pack(codes))
+    s = synth.scales(N, K, workload=90, matrix=N)
+    w = gu.pack_dev(codes, s)
+    torch.cuda.synchronize()
+    wq_t, sc_t = oracle.pack_tiled(codes, s)
+    assert np.array_equal(w.codes.cpu().numpy(), wq_t)
+    assert np.array_equal(w.scales.view(torch.int16).cpu().numpy().view(np.uint16), sc_t)
 
 
 def test_pack_ignores_high_bits_and_unaligned_source():
@@ -33,8 +39,12 @@ def test_pack_ignores_high_bits_and_unaligned_source():
     rng = np.random.default_rng(5)
     N, K = 9, 160
     raw = rng.integers(0, 256, size=N * K + 1, dtype=np.uint8)
+    s = oracle_pins.random_scale_bits(rng, (N, K // 32))
     dev = gu.u8_to_dev(raw)
     codes_dev = dev[1:].view(N, K)          # 1-byte offset: unaligned source
-    got = q4.pack(codes_dev).cpu().numpy()
-    assert np.array_equal(got, oracle.pack(raw[1:].reshape(N, K)))
-    assert np.array_equal(oracle.unpack(got, K), raw[1:].reshape(N, K) & 0x0F)
+    w = q4.pack(codes_dev, gu.scales_to_dev(s))
+    torch.cuda.synchronize()
+    wq_t, sc_t = oracle.pack_tiled(raw[1:].reshape(N, K), s)
+    assert np.array_equal(w.codes.cpu().numpy(), wq_t)
+    c2, s2 = oracle.unpack_tiled(w.codes.cpu().numpy(), w.scales.view(torch.int16).cpu().numpy(), N, K)
+    assert np.array_equal(c2, raw[1:].reshape(N, K) & 0x0F) and np.array_equal(s2, s)
