@@ -26,11 +26,12 @@
  *   - The library's tiled layout (what its pack produces and its kernels
  *     read): tiles of 16 rows (t = n / 16, c = n % 16) by 4 blocks
  *     (q = b / 4, i = b % 4), ordered [ceil(N/16)][ceil(nb/4)], 1024 code
- *     bytes and 64 scales each.  Inside a code tile, the byte at
- *     16 * (16 g + c) + 4 i + j is canonical byte 4 g + j of block b of row
- *     n (the codes of k = 32 b + 8 g + 2 j and k + 1, g, j in 0..3).  The
- *     scale of (n, b) is element 4 c + i of its tile's 64.  Positions past
- *     N rows or nb blocks are zero.
+ *     bytes and 64 scales each.  Inside a code tile, the little-endian
+ *     32-bit word at byte 16 * (16 g + c) + 4 i holds the eight codes of
+ *     k = 32 b + 8 g + r, r = 0..7, of row n: the code of r sits at bit
+ *     4 * (r / 2) + 16 * (r % 2) (even r in the low half-word, odd r in the
+ *     high one, each half in ascending r).  The scale of (n, b) is element
+ *     4 c + i of its tile's 64.  Positions past N rows or nb blocks are zero.
  *
  * Definition computed (the plain reading):
  *     y[m][n] = sum_{k=0}^{K-1} x[m][k] * (q[n][k] - 8) * d[n][k/32]
@@ -47,7 +48,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#define Q4O_ABI 1
+#define Q4O_ABI 2
 
 int q4o_abi_version(void) { return Q4O_ABI; }
 
@@ -99,11 +100,18 @@ static int code_at(const uint8_t *wq, int64_t K, int64_t n, int64_t k)
  * weight (n, k) and block (n, b). */
 static int64_t quads_of(int64_t K) { return (K / 32 + 3) / 4; }
 
-static int64_t tiled_byte_index(int64_t K, int64_t n, int64_t k)
+/* Word index (in 32-bit words) and bit position of weight (n, k)'s code. */
+static int64_t tiled_word_index(int64_t K, int64_t n, int64_t k)
 {
-    const int64_t b = k / 32, g = (k % 32) / 8, j = (k % 8) / 2;
+    const int64_t b = k / 32, g = (k % 32) / 8;
     const int64_t t = n / 16, c = n % 16, q = b / 4, i = b % 4;
-    return (t * quads_of(K) + q) * 1024 + 16 * (16 * g + c) + 4 * i + j;
+    return ((t * quads_of(K) + q) * 1024 + 16 * (16 * g + c) + 4 * i) / 4;
+}
+
+static int tiled_bit(int64_t k)
+{
+    const int r = (int)(k % 8);
+    return 4 * (r / 2) + 16 * (r % 2);
 }
 
 static int64_t tiled_scale_index(int64_t K, int64_t n, int64_t b)
@@ -112,10 +120,16 @@ static int64_t tiled_scale_index(int64_t K, int64_t n, int64_t b)
     return (t * quads_of(K) + q) * 64 + 4 * c + i;
 }
 
+/* The 32-bit word at word index w of a tiled code buffer (little-endian). */
+static uint32_t tiled_word(const uint8_t *wq, int64_t w)
+{
+    return (uint32_t)wq[4 * w] | ((uint32_t)wq[4 * w + 1] << 8) | ((uint32_t)wq[4 * w + 2] << 16) |
+           ((uint32_t)wq[4 * w + 3] << 24);
+}
+
 static int tiled_code_at(const uint8_t *wq, int64_t K, int64_t n, int64_t k)
 {
-    const uint8_t byte = wq[tiled_byte_index(K, n, k)];
-    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return (int)((tiled_word(wq, tiled_word_index(K, n, k)) >> tiled_bit(k)) & 0x0F);
 }
 
 /* Dequantized weight (n, k) = (q - 8) * d[n][k/32], exact in fp64. */
@@ -162,10 +176,11 @@ void q4o_pack_tiled(const uint8_t *codes, const uint16_t *scales, uint8_t *wq_t,
     for (int64_t i = 0; i < q4o_tiled_scale_count(N, K); ++i)
         sc_t[i] = 0;
     for (int64_t n = 0; n < N; ++n) {
-        for (int64_t k = 0; k < K; k += 2) {
-            const uint8_t lo = codes[n * K + k] & 0x0F;
-            const uint8_t hi = codes[n * K + k + 1] & 0x0F;
-            wq_t[tiled_byte_index(K, n, k)] = (uint8_t)(lo | (hi << 4));
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t w = tiled_word_index(K, n, k);
+            const int bit = tiled_bit(k);
+            const uint8_t code = codes[n * K + k] & 0x0F;
+            wq_t[4 * w + bit / 8] |= (uint8_t)(code << (bit % 8));
         }
         for (int64_t b = 0; b < K / 32; ++b)
             sc_t[tiled_scale_index(K, n, b)] = scales[n * (K / 32) + b];

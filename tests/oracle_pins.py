@@ -211,16 +211,20 @@ def pin_pack(lib, seed: int = 3) -> None:
 
 def np_pack_tiled(codes: np.ndarray, scales: np.ndarray):
     """The tiled layout built with numpy reshapes: pad to 16 rows and 4-block
-    quads, pack nibbles canonically, then order (tile, quad, g, row, block, j)."""
+    quads, gather each lane's eight codes (k = 32 b + 8 g + r) into one
+    little-endian 32-bit word with code r at bit 4 (r // 2) + 16 (r % 2),
+    then order the words (tile, quad, g, row, block)."""
     N, K = codes.shape
     nb = K // 32
     n16 = -(-N // 16) * 16
     nb4 = -(-nb // 4) * 4
     Q = nb4 // 4
-    c = np.zeros((n16, nb4 * 32), np.uint8)
+    c = np.zeros((n16, nb4 * 32), np.uint32)
     c[:N, :K] = np.asarray(codes, np.uint8) & 0x0F
-    byt = (c[:, 0::2] | (c[:, 1::2] << 4)).reshape(n16 // 16, 16, Q, 4, 4, 4)  # t, row, q, i, g, j
-    wq = byt.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+    r = np.arange(8)
+    shifts = (4 * (r // 2) + 16 * (r % 2)).astype(np.uint32)
+    words = (c.reshape(n16 // 16, 16, Q, 4, 4, 8) << shifts).sum(axis=-1, dtype=np.uint32)  # t, row, q, i, g
+    wq = np.ascontiguousarray(words.transpose(0, 2, 4, 1, 3)).astype("<u4").view(np.uint8).reshape(-1)
     s = np.zeros((n16, nb4), np.uint16)
     s[:N, :nb] = scales
     sc = s.reshape(n16 // 16, 16, Q, 4).transpose(0, 2, 1, 3).reshape(-1)

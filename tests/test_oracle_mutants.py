@@ -20,9 +20,9 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "q4_oracle.c")
 MUTANTS = {
     "nibble_order": ("k / 2];\n    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
                      "k / 2];\n    return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
-    "tiled_nibble_order": ("(K, n, k)];\n    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
-                           "(K, n, k)];\n    return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    "tiled_nibble_order": ("return 4 * (r / 2) + 16 * (r % 2);", "return 4 * (r % 4) + 16 * (r / 4);"),
     "tiled_lane_order": ("16 * (16 * g + c)", "16 * (4 * c + g)"),
+    "tiled_word_endian": ("((uint32_t)wq[4 * w + 3] << 24)", "((uint32_t)wq[4 * w + 3] << 16)"),
     "tiled_scale_order": ("* 64 + 4 * c + i", "* 64 + 16 * i + c"),
     "tiled_quad_stride": ("(t * quads_of(K) + q) * 1024", "(q * ((n + 15) / 16 + 1) + t) * 1024"),
     "offset_7": ("(double)(q - 8)", "(double)(q - 7)"),
@@ -37,7 +37,7 @@ MUTANTS = {
     "bf16_bias": ("expo - 134)", "expo - 133)"),
     "pack_shift": ("wq[n * (K / 2) + j] = (uint8_t)(lo | (hi << 4));",
                    "wq[n * (K / 2) + j] = (uint8_t)(lo | (hi << 3));"),
-    "tiled_pack_shift": ("(K, n, k)] = (uint8_t)(lo | (hi << 4));", "(K, n, k)] = (uint8_t)(lo | (hi << 3));"),
+    "tiled_pack_shift": ("(uint8_t)(code << (bit % 8));", "(uint8_t)(code << (bit % 4));"),
     "abs_dropped": ("mag += fabs(t);", "mag += t;"),
 }
 
