@@ -37,7 +37,7 @@ EXPORTS = (
     "q4_last_hip_error", "q4_abi_version",
 )
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class Q4Error(RuntimeError):

@@ -64,6 +64,11 @@ int check_shape(long long M, long long N, long long K)
 {
     if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
         return Q4_ERR_SHAPE;
+    // one column tile's packed codes (K / 2 * 16 bytes) and 16 rows of x
+    // (32 K bytes) stay below 2^31 bytes: the kernels address them with
+    // 32-bit offsets
+    if (K > (1LL << 25))
+        return Q4_ERR_SHAPE;
     // every element count must fit comfortably in 63 bits and every row
     // index product used by the kernels in size_t
     const long long lim = 1LL << 46;

@@ -9,27 +9,32 @@
 // kernels summed in different orders and dequantized at different times, so
 // a batching decision changed the numbers written to the KV cache.
 //
-// The order (version 1), for output (m, n), K = 32 * nb:
+// The order (version 2), for output (m, n), K = 32 * nb:
 //   quads:    G = ceil(nb / 4) groups of 4 blocks; the last may be short.
 //   segments: S = min(16, 2^floor(log2 G)); segment j covers quads
 //             [floor(j G / S), floor((j+1) G / S)), i.e. blocks
 //             [4 floor(j G / S), min(nb, 4 floor((j+1) G / S))).
-//   block dot: s_b = element (m, n) of ONE v_mfma_f32_16x16x32_{bf16,f16}
-//             with C = 0, A row = x[m][32b .. 32b+31] in natural k order,
-//             B column = (q[n][32b+k] - 8) / 16, exact in x's 16-bit type.
+//   block dot: s_b = fl(D - E) for element (m, n) of two
+//             v_mfma_f32_16x16x32_{bf16,f16} with C = 0 and A row =
+//             x[m][32b .. 32b+31] in natural k order: D with B column =
+//             V + q[n][32b+k], E with every B entry = V + 8, where V = 128
+//             (bf16) or 1024 (fp16).  Both B operands are exact in x's type,
+//             so s_b approximates sum_k x (q - 8); a block of all-8 codes
+//             gives D = E and s_b = 0 exactly.  E depends on x only.
 //   segment:  p_j = +0; for b ascending: p_j = fmaf(d[n][b], s_b, p_j).
 //   tree:     for h = 1, 2, 4, .. S/2: p_j = p_j + p_{j+h} for j % 2h == 0.
-//   output:   y[m][n] = 16 * p_0   (exact: undoes the 1/16 of the operand).
+//   output:   y[m][n] = p_0.
 // S depends on K only, so slicing N (sharding) keeps every bit.
 //
 // Weight layout read by the kernels (written by q4_pack): tiles of 16
 // columns (t = n / 16, c = n % 16) by one quad (q = b / 4, i = b % 4),
 // ordered [ceil(N/16)][G].  A tile holds 1024 code bytes, 16 per lane of a
-// wave in lane order l = 16 g + c: bytes 4 i .. 4 i + 3 of lane l are bytes
-// 4 g .. 4 g + 3 of block 4 q + i of column n in the row-major packing
-// (codes of k = 32 b + 8 g .. + 7, low nibble first).  So one 16-byte load
-// gives lane (g, c) exactly the B-operand dwords of the tile's four block
-// dots.  Then 64 fp16 scales, [c][i].  Padding (n >= N, b >= nb) is zero.
+// wave in lane order l = 16 g + c: the little-endian word at bytes 4 i ..
+// 4 i + 3 of lane l holds the codes of column n, k = 32 b + 8 g + r,
+// r = 0..7, with code r at bit 4 (r / 2) + 16 (r % 2).  So one 16-byte load
+// gives lane (g, c) its B-operand codes of the tile's four block dots, and
+// a mask-and-or per pair of k turns them into operand words.  Then 64 fp16
+// scales, [c][i].  Padding (n >= N, b >= nb) is zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,37 +52,56 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- dequant
-// v_cvt_off_f32_i4 reads bits 3..0 of its source as a signed 4-bit integer
-// t and returns t / 16.  With t = q ^ 8, t is q - 8 in two's complement, so
-// each call yields (q - 8) / 16 exactly.  Only the compiler builtin is used
-// (no inline assembly): the compiler then tracks every register the
-// conversions write against in-flight matrix-core instructions.
-__device__ __forceinline__ float i4_at(uint32_t v) { return __builtin_amdgcn_cvt_off_f32_i4((int)v); }
-
+// The 16-bit pattern (V_BITS | q), q in 0..15, is V + q exactly: V = 128 in
+// bf16 (0x4300; the ulp on [128, 256) is 1) and V = 1024 in fp16 (0x6400).
 template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+constexpr uint32_t kMagic = BF16 ? 0x43004300u : 0x64006400u;
+// B operand of the correction dot E: V + 8 in every entry.
+template <bool BF16>
+constexpr uint32_t kOffset = BF16 ? 0x43084308u : 0x64086408u;
+
+// One packed word (code r at bit 4 (r / 2) + 16 (r % 2)) -> the eight
+// operand values V + q in natural k order, two per dword: one mask-and-or
+// per dword.  mask = 0x000F000F and magic = kMagic must arrive as opaque
+// registers (see Dequant): as literals the compiler splits each step in two
+// (this target's three-operand instructions take no literal).
+template <bool BF16>
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, uint32_t mask, uint32_t magic)
 {
-    if constexpr (BF16) {
-        const bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32; exact here
-        return __builtin_bit_cast(uint32_t, v);
-    } else {
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));  // exact here
-    }
+    u32x4 r;
+    r.x = (w & mask) | magic;
+    r.y = ((w >> 4) & mask) | magic;
+    r.z = ((w >> 8) & mask) | magic;
+    r.w = ((w >> 12) & mask) | magic;
+    return r;
 }
 
-// Eight codes (one packed dword: code of k = i in bits 4i..4i+3) -> the
-// eight operand values (q - 8)/16 in natural k order, two per dword.
+// The dequant constants in registers the compiler cannot fold: the mask in a
+// scalar register, the magic in a vector one (one scalar operand per
+// instruction on this target).  The empty statements emit no instructions.
+// The correction's B operand (V + 8 everywhere) is built once the same way,
+// so the compiler keeps it in four registers instead of rebuilding it for
+// every block dot.
 template <bool BF16>
-__device__ __forceinline__ u32x4 dequant8(uint32_t w)
+struct Dequant {
+    uint32_t mask, magic;
+    u32x4 offset;
+    __device__ __forceinline__ Dequant()
+    {
+        mask = 0x000F000Fu;
+        magic = kMagic<BF16>;
+        offset = (u32x4){kOffset<BF16>, kOffset<BF16>, kOffset<BF16>, kOffset<BF16>};
+        asm volatile("" : "+s"(mask));
+        asm volatile("" : "+v"(magic));
+        asm volatile("" : "+v"(offset));
+    }
+    __device__ __forceinline__ u32x4 operator()(uint32_t w) const { return dequant8<BF16>(w, mask, magic); }
+};
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 offset_operand()
 {
-    const uint32_t t = w ^ 0x88888888u;
-    const uint32_t h = (w >> 4) ^ 0x08888888u;
-    u32x4 r;
-    r.x = pack2<BF16>(i4_at(t), i4_at(h));
-    r.y = pack2<BF16>(i4_at(t >> 8), i4_at(h >> 8));
-    r.z = pack2<BF16>(i4_at(t >> 16), i4_at(h >> 16));
-    r.w = pack2<BF16>(i4_at(t >> 24), i4_at(h >> 24));
-    return r;
+    return (u32x4){kOffset<BF16>, kOffset<BF16>, kOffset<BF16>, kOffset<BF16>};
 }
 
 // ---------------------------------------------------------------- BlockDot
@@ -101,43 +125,55 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// p = fmaf(d, s, p) for the four accumulator rows a lane holds.
-__device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 s)
+// p = fmaf(d, D - E, p) for the four accumulator rows a lane holds (the
+// difference rounds first: -ffp-contract=off keeps it a separate step).
+__device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 D, f32x4 E)
 {
-    p.x = __builtin_fmaf(d, s.x, p.x);
-    p.y = __builtin_fmaf(d, s.y, p.y);
-    p.z = __builtin_fmaf(d, s.z, p.z);
-    p.w = __builtin_fmaf(d, s.w, p.w);
+    p.x = __builtin_fmaf(d, D.x - E.x, p.x);
+    p.y = __builtin_fmaf(d, D.y - E.y, p.y);
+    p.z = __builtin_fmaf(d, D.z - E.z, p.z);
+    p.w = __builtin_fmaf(d, D.w - E.w, p.w);
 }
 
 // Streaming form of the pairwise tree for one wave that owns an aligned run
-// of L segments (L a power of two, at most 2^LV): call after each finished
-// segment li = 0..L-1 with its partial in cur.  Left subtrees wait in stack
-// (a binary counter over li); after li = L-1, cur holds the run's subtree
-// root and the call returns true.  Otherwise cur must restart from +0.
-template <int LV, int NACC>
-__device__ __forceinline__ bool tree_push(f32x4 (&stack)[LV][NACC], f32x4 (&cur)[NACC], int li, int L)
-{
-    int lvl = 0;
+// of L <= 16 segments (L a power of two): push() after each finished
+// segment li = 0..L-1 with its partial in cur.  Left subtrees wait at the
+// levels: the trailing one-bits of li name the levels that merge into cur
+// (left operand first), the first zero-bit the level cur then waits at.
+// After li = L-1, cur holds the run's subtree root and push() returns true;
+// otherwise cur must restart from +0.  The levels are separate named
+// registers written by value (selects), never through an index or a
+// pointer, so they cannot fall back to scratch memory.
+template <int NACC, typename T>
+struct TreeStack {
+    T s0[NACC], s1[NACC], s2[NACC], s3[NACC];
+
+    __device__ __forceinline__ bool push(T (&cur)[NACC], int li, int L)
+    {
+        const bool m0 = li & 1, m1 = m0 && (li & 2), m2 = m1 && (li & 4), m3 = m2 && (li & 8);
 #pragma unroll
-    for (int l = 0; l < LV; ++l) {
-        if (lvl == l && ((li >> l) & 1)) {
-#pragma unroll
-            for (int a = 0; a < NACC; ++a)
-                cur[a] = stack[l][a] + cur[a];
-            lvl = l + 1;
+        for (int a = 0; a < NACC; ++a) {
+            if (m0)
+                cur[a] = s0[a] + cur[a];
+            if (m1)
+                cur[a] = s1[a] + cur[a];
+            if (m2)
+                cur[a] = s2[a] + cur[a];
+            if (m3)
+                cur[a] = s3[a] + cur[a];
         }
+        const bool root = li == L - 1;
+        const bool w0 = !root && !m0, w1 = !root && m0 && !m1, w2 = !root && m1 && !m2, w3 = !root && m2 && !m3;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) {
+            s0[a] = w0 ? cur[a] : s0[a];
+            s1[a] = w1 ? cur[a] : s1[a];
+            s2[a] = w2 ? cur[a] : s2[a];
+            s3[a] = w3 ? cur[a] : s3[a];
+        }
+        return root;
     }
-    if ((1 << lvl) >= L)
-        return true;
-#pragma unroll
-    for (int l = 0; l < LV; ++l)
-        if (l == lvl)
-#pragma unroll
-            for (int a = 0; a < NACC; ++a)
-                stack[l][a] = cur[a];
-    return false;
-}
+};
 
 // Pairwise tree over v[0..S): the fixed order of the contract.
 template <int SMAX>

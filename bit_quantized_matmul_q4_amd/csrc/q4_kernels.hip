@@ -33,206 +33,309 @@
 namespace q4 {
 
 // =================================================================== GEMV
-// One ring stage: a quad of T column tiles as loaded.  Lane (g, c) holds per
-// tile the B-operand dwords of the four block dots and the column's four
-// scales, plus its A-operand slice (row slot c, k-slots 8g..8g+7) of each of
-// the four blocks, shared by the T tiles.
-template <int T>
+// Buffer resource over a wave-uniform base.  Every offset below is kept in
+// range by construction (clamped stream indices); the resource form lets the
+// per-load offsets live in scalar registers, so streaming costs no vector
+// address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes = 0xFFFFFFFFu)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One ring stage: one tile-quad of the wave's stream as loaded.  Lane (g, c)
+// holds the B-operand dwords of the quad's four block dots, its column's four
+// scales and its A-operand slice (row slot c, k-slots 8g..8g+7) of the four
+// blocks of x.
+constexpr int GEMV_TPS_MAX = 8;  // column tiles per stream (outputs staged in LDS)
+
 struct GemvStage {
-    u32x4 codes[T];
-    u32x2 sc[T];
+    u32x4 w;
+    u32x2 s;
     u32x4 xa[4];
 };
 
-// Unconditional loads: the quad index is clamped by the caller, blocks past
-// nb re-read block nb-1 of x (their MFMAs are skipped), and row slots past M
-// re-read the last row (those outputs are never stored; an MFMA output
-// element depends only on its own A row and B column).
-template <int T>
-__device__ __forceinline__ void gemv_load(GemvStage<T> &S, const uint8_t *wt, const uint16_t *st,
-                                          size_t tile_bytes, size_t tile_scales,
-                                          const uint16_t *xrow, int q, int nb)
+// R: accumulator components that can hold real batch rows (min(rows, 4),
+// compile-time).  nq: blocks in the quad (4 except a short last quad).
+template <bool BF16, int R, bool SHORT>
+__device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)[4], int nq, const Dequant<BF16> &dq,
+                                          float (&p)[R])
 {
+    const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+    const uint32_t h[4] = {st.s.x & 0xFFFFu, st.s.x >> 16, st.s.y & 0xFFFFu, st.s.y >> 16};
+    // the block dots first, so their matrix-core latencies overlap
+    f32x4 D[4], E[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        S.codes[t] = *(const u32x4 *)(wt + t * tile_bytes + (size_t)q * 1024);
-        S.sc[t] = *(const u32x2 *)(st + t * tile_scales + (size_t)q * 64);
+    for (int i = 0; i < 4; ++i) {
+        D[i] = blockdot<BF16>(xa[i], dq(w[i]));
+        E[i] = blockdot<BF16>(xa[i], dq.offset);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        S.xa[i] = *(const u32x4 *)(xrow + (size_t)min(4 * q + i, nb - 1) * 32);
-}
-
-// R: accumulator registers that can hold real batch rows (min(rows, 4), a
-// compile-time count so no per-register test reaches the hot loop).
-// NQ: blocks in the quad (4, or fewer only for the last quad of K).
-template <bool BF16, int T, int R>
-__device__ __forceinline__ void gemv_compute(const GemvStage<T> &S, int nq, f32x4 (&p)[T])
-{
+    for (int i = 0; i < 4; ++i) {
+        if (!SHORT || i < nq) {
+            const float d = half_bits_to_float(h[i]);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const uint32_t w[4] = {S.codes[t].x, S.codes[t].y, S.codes[t].z, S.codes[t].w};
-        const uint32_t h[4] = {S.sc[t].x & 0xFFFFu, S.sc[t].x >> 16, S.sc[t].y & 0xFFFFu, S.sc[t].y >> 16};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < nq) {
-                const float d = half_bits_to_float(h[i]);
-                const f32x4 s = blockdot<BF16>(S.xa[i], dequant8<BF16>(w[i]));
-                p[t].x = __builtin_fmaf(d, s.x, p[t].x);
-                if constexpr (R > 1)
-                    p[t].y = __builtin_fmaf(d, s.y, p[t].y);
-                if constexpr (R > 2)
-                    p[t].z = __builtin_fmaf(d, s.z, p[t].z);
-                if constexpr (R > 3)
-                    p[t].w = __builtin_fmaf(d, s.w, p[t].w);
-            }
+            for (int r = 0; r < R; ++r)
+                p[r] = __builtin_fmaf(d, D[i][r] - E[i][r], p[r]);
         }
     }
 }
 
-// End of segment li of a run of L (1 or 4) segments: the pairwise tree
-// of the run, written out.  After the run's last segment p holds the root.
-// Each case is a real (uniform) branch: the empty asm keeps the compiler
-// from turning the merges into per-quad selects.
-template <int T, int L>
-__device__ __forceinline__ void gemv_segment_done(int li, f32x4 (&p)[T], f32x4 (&s0)[T], f32x4 (&s1)[T])
+// The wave's stream is a contiguous run of tile-quads: quad i of the stream
+// sits at code byte 1024 i and scale byte 128 i from the wave's base, and is
+// quad q0 + (i mod RQ) of K.  The code and scale resources span exactly the
+// stream, and the range check covers the scalar offset: the ring's refills
+// past the end return zero without a memory access, with no clamp or test.
+// x blocks past nb (a short last quad) read whatever follows (the next row,
+// or zero past the slice); their block dots are skipped.
+struct GemvStream {
+    __amdgpu_buffer_rsrc_t w, s, x;
+    uint32_t w_lane, s_lane, x_lane;  // per-lane byte offsets
+    uint32_t w_off, s_off;            // scalar offsets of the next refill
+};
+
+// Keeps the ring's loads in program order relative to their uses: the empty
+// statement (no instructions) with a memory clobber stops IR-level motion,
+// the scheduling barrier stops the machine scheduler.
+__device__ __forceinline__ void issue_fence()
 {
-    static_assert(L == 1 || L == 4, "runs of 1 or 4 segments");
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (L == 1)
-        return;
-    switch (li) {  // L == 4: ((p0 + p1) + (p2 + p3))
-    case 0:
-        asm volatile("");
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            s0[t] = p[t];
-            p[t] = zero;
-        }
-        break;
-    case 1:
-        asm volatile("");
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            s1[t] = s0[t] + p[t];
-            p[t] = zero;
-        }
-        break;
-    case 2:
-        asm volatile("");
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            s0[t] = p[t];
-            p[t] = zero;
-        }
-        break;
-    default:
-        asm volatile("");
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-            p[t] = s1[t] + (s0[t] + p[t]);
-        break;
-    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
-// grid = (ceil(N / (16 T)), ceil(M / 16)), block = 64 * Wc threads with
-// Wc = S / L.  Wave w owns the aligned run of L segments starting at segment
-// w L.  SHORT: K/32 is not a multiple of 4, so the last quad of K has fewer
-// than four blocks.  Dynamic LDS: Wc * T * 16 * 17 floats (subtree roots).
-template <bool BF16, int T, int D, int R, int L, bool SHORT>
-__global__ __launch_bounds__(1024) void q4_gemv(const uint16_t *__restrict__ x,
-                                                const uint8_t *__restrict__ wq,
-                                                const uint16_t *__restrict__ scales,
-                                                float *__restrict__ y, int M, int N, int K, Plan plan)
+// Loads one stage: the next quad of the stream and, unless x is staged in
+// LDS (XL), the x blocks of quad x_off / 256 (x_off >= the slice size for a
+// refill past the stream's end).
+template <bool XL>
+__device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
-    extern __shared__ float red_lds[];  // [wave][tile][row slot][column slot (17)]
+    st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane, in.w_off, 0));
+    st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane, in.s_off, 0));
+    if constexpr (!XL) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            st.xa[b] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b, x_off, 0));
+    }
+    in.w_off += 1024;
+    in.s_off += 128;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int Wc = blockDim.x >> 6;
-    const int g = lane >> 4;   // lane group: k-slots 8g..8g+7, output rows 4g..4g+3
-    const int c = lane & 15;   // column slot (B, D) and row slot (A)
+// A-operand slice of quad q from the x rows staged in LDS (lane row base
+// xrow, 16 g already added): four 16-byte reads.
+__device__ __forceinline__ void gemv_x_lds(u32x4 (&xa)[4], const uint8_t *xrow, int q)
+{
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        xa[b] = *(const u32x4 *)(xrow + 256 * q + 64 * b);
+}
+
+// Bytes of LDS a row of x takes when staged: padded by 16 so that rows start
+// in different banks.
+__host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t)K * 2u + 16u; }
+
+// grid = (streams / 4 or column tiles, ceil(M / 16)).
+//  SPLIT = false: block = 256; each wave streams `tps` consecutive column
+//    tiles over all of K (one run of S segments) and stores each tile's
+//    outputs itself.
+//  SPLIT = true: block = 64 W with W = S / L <= 8; workgroup = one column tile,
+//    wave w streams run w (segments w L .. w L + L - 1); the W run roots meet
+//    in LDS for the top of the pairwise tree.
+//  XL: the workgroup first copies its x rows into LDS and every wave reads its
+//    A operands there; otherwise each stage loads them with the weights.
+//    Every wave of every workgroup reads the same few kilobytes of x, so as
+//    per-quad loads they become a stream of requests to the same few cache
+//    lines, which costs as much as the weights themselves.
+// Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
+// (XL) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of slack.
+template <bool BF16, int R, int D, bool SHORT, bool SPLIT, bool XL>
+__global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x,
+                                                              const uint8_t *__restrict__ wq,
+                                                              const uint16_t *__restrict__ scales,
+                                                              float *__restrict__ y, int M, int N, int K,
+                                                              Plan plan, int L, int tps)
+{
+    // SPLIT: the run roots, [wave][row slot][column slot (17)].  Otherwise the
+    // stream's tile roots (dynamic LDS): a store inside the streaming loop
+    // would make every wait on the ring drain the whole ring (loads and
+    // stores share one counter), so y is written after it.
+    __shared__ float red[SPLIT ? 8 * 16 * 17 : 1];
+    extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
+    float *ystage = dyn_lds;
+    uint8_t *xlds = (uint8_t *)(dyn_lds + (SPLIT ? 0 : 4 * tps * 256));
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;  // k-slots 8g..8g+7 (A, B); output rows 4g..4g+3 (D)
+    const int c = lane & 15;  // row slot (A); column slot (B, D)
     const int n16 = (N + 15) / 16;
-    const int tile0 = blockIdx.x * T;
+    const int G = plan.G;
     const int m0 = blockIdx.y * 16;
     const int mrows = min(16, M - m0);
-    const int G = plan.G;
 
-    // tiles past the last one re-read the last tile (never stored)
-    const size_t tile_bytes = (size_t)G * 1024;
-    const size_t tile_scales = (size_t)G * 64;
-    const int tfirst = min(tile0, n16 - 1);
-    const uint8_t *wt = wq + (size_t)tfirst * tile_bytes + 16 * lane;
-    const uint16_t *st = scales + (size_t)tfirst * tile_scales + 4 * c;
-    size_t tstep_b = tile_bytes, tstep_s = tile_scales;
-    if (tile0 + T > n16) {  // partial tile group at the end: all T tiles read the last one
-        tstep_b = 0;
-        tstep_s = 0;
+    int t0, ntiles, run;
+    if constexpr (SPLIT) {
+        t0 = blockIdx.x;
+        ntiles = 1;
+        run = wave;
+    } else {
+        t0 = (blockIdx.x * 4 + wave) * tps;
+        ntiles = max(0, min(tps, n16 - t0));  // 0: a spare wave of the last workgroup
+        run = 0;
+        if (!XL && ntiles == 0)
+            return;  // no barrier follows in this form
     }
-    const uint16_t *xrow = x + (size_t)(m0 + min(c, mrows - 1)) * K + 8 * g;
+    const int seg0 = run * L;
+    const int q0 = (seg0 * G) >> plan.log2S;
+    const int q1 = ((seg0 + L) * G) >> plan.log2S;
+    const int total = ntiles * (q1 - q0);
 
-    const int seg0 = wave * L;
-    const int q0 = (seg0 * G) >> plan.log2S;              // first quad of the run
-    const int q1 = ((seg0 + L) * G) >> plan.log2S;        // end quad of the run
-    const int qlast = q1 - 1;
-    int li = 0;                                           // segment within the run
-    int seg_end_q = ((seg0 + 1) * G) >> plan.log2S;       // end quad of the current segment
+    const uint32_t x_bytes = (uint32_t)mrows * (uint32_t)K * 2u;
+    GemvStream in;
+    in.w = buffer_rsrc(wq + ((size_t)min(t0, n16 - 1) * G + q0) * 1024, (uint32_t)total * 1024u);
+    in.s = buffer_rsrc(scales + ((size_t)min(t0, n16 - 1) * G + q0) * 64, (uint32_t)total * 128u);
+    in.x = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
+    in.w_lane = 16u * lane;
+    in.s_lane = 8u * c;
+    in.x_lane = (uint32_t)min(c, mrows - 1) * (uint32_t)K * 2u + 16u * g;
+    in.w_off = 0;
+    in.s_off = 0;
 
-    f32x4 p[T], s0[T], s1[T];
+    GemvStage ring[D];
+    int ql = q0;     // quad of the next stage to load
+    int left = total;  // loads left that the stream uses
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        p[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    GemvStage<T> ring[D];
+    for (int d = 0; d < D; ++d) {  // in stage order (see the refill below)
+        gemv_load<XL>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+        ql = ql + 1 == q1 ? q0 : ql + 1;
+        --left;
+        issue_fence();
+    }
+    const uint8_t *xrow = xlds + (uint32_t)min(c, mrows - 1) * gemv_xrow_bytes(K) + 16 * g;
+    if constexpr (XL) {
+        // copy the x rows into LDS, 16 bytes per thread and step, in rounds
+        // of 8 loads so that each round costs one memory round trip
+        const int cpr = K / 8;  // 16-byte chunks per row
+        const int nch = mrows * cpr;
+        for (int i0 = 0; i0 < nch; i0 += 8 * (int)blockDim.x) {
+            u32x4 v[8];
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        gemv_load<T>(ring[d], wt, st, tstep_b, tstep_s, xrow, min(q0 + d, qlast), plan.nb);
-
-    for (int q = q0; q < q1; q += D) {
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + u * (int)blockDim.x + (int)threadIdx.x, nch - 1);
+                const int r = i / cpr;
+                v[u] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, (uint32_t)i * 16u, 0, 0));
+                (void)r;
+            }
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int qq = q + d;
-            if (qq < q1) {
-                if constexpr (SHORT)
-                    gemv_compute<BF16, T, R>(ring[d], min(4, plan.nb - 4 * qq), p);
-                else
-                    gemv_compute<BF16, T, R>(ring[d], 4, p);
-                if (qq + 1 == seg_end_q) {  // segment finished: fold into the run's subtree
-                    gemv_segment_done<T, L>(li, p, s0, s1);
-                    ++li;
-                    seg_end_q = ((seg0 + li + 1) * G) >> plan.log2S;
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+                if (i < nch) {
+                    const int r = i / cpr;
+                    *(u32x4 *)(xlds + (uint32_t)r * gemv_xrow_bytes(K) + (uint32_t)(i - r * cpr) * 16u) = v[u];
                 }
             }
-            // refill this stage D quads ahead (clamped: past the run it
-            // re-reads the run's last quad, an L2 hit)
-            gemv_load<T>(ring[d], wt, st, tstep_b, tstep_s, xrow, min(qq + D, qlast), plan.nb);
+        }
+        __syncthreads();
+    }
+    // The compiler may reorder the prefill's loads (it clusters loads from
+    // one base).  Waiting for all of them here costs little (they were issued
+    // together and the first compute needs the first of them) and keeps that
+    // order from pessimising every wait of the loop, whose header merges the
+    // prefill's pending loads with the refills'.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    const Dequant<BF16> dq;
+    // accumulators: the R rows a lane can hold (rows 4g .. 4g + R - 1)
+    float p[R], root[R];
+    TreeStack<R, float> stack;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        p[r] = root[r] = 0.f;
+    int qc = q0;  // quad being computed
+    int t = 0;    // its tile, counted from t0
+    int li = 0;   // segment within the run
+    int seg_end = ((seg0 + 1) * G) >> plan.log2S;
+    u32x4 xb[2][4];  // XL: x of the quad being computed and of the next
+    if constexpr (XL)
+        gemv_x_lds(xb[0], xrow, q0);
+    for (int base = 0; base < total; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int ii = base + d;
+            if (ii < total) {
+                const int qn = qc + 1 == q1 ? q0 : qc + 1;
+                if constexpr (XL)
+                    gemv_x_lds(xb[(d + 1) & 1], xrow, qn);
+                gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
+                                          SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                if (qc + 1 == seg_end) {  // segment done: fold into the run's subtree
+                    if (stack.push(p, li, L)) {
+                        if constexpr (SPLIT) {
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+                                root[r] = p[r];
+                        } else {  // the tile's root, kept in LDS until the stream ends
+                            float *o = ystage + ((wave * tps + t) * 16 + 4 * g) * 16 + c;
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+                                o[16 * r] = p[r];
+                            ++t;
+                        }
+                        li = 0;
+                    } else {
+                        ++li;
+                    }
+                    seg_end = ((seg0 + li + 1) * G) >> plan.log2S;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        p[r] = 0.f;
+                }
+                qc = qn;
+            }
+            // refill D quads ahead.  The scheduling barrier keeps the refill
+            // after the stage's use: hoisted above it, the refill's wait (the
+            // memory counter retires in order) would drain the whole ring.
+            // Refills past the stream's end fall outside the resources'
+            // ranges: they return zero without a memory access, so the
+            // wave's end does not wait one more round trip for them.
+            issue_fence();
+            gemv_load<XL>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+            ql = ql + 1 == q1 ? q0 : ql + 1;
+            --left;
+            issue_fence();
         }
     }
 
+    if constexpr (!SPLIT) {  // y = root for the stream's tiles
+        for (int k = 0; k < ntiles; ++k) {
+            const int n = 16 * (t0 + k) + c;
+            if (n >= N)
+                break;
+            const float *o = ystage + ((wave * tps + k) * 16 + 4 * g) * 16 + c;
+            float *yo = y + (size_t)(m0 + 4 * g) * N + n;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float *r = red_lds + ((wave * T + t) * 16) * 17;
-        r[(4 * g + 0) * 17 + c] = p[t].x;
-        r[(4 * g + 1) * 17 + c] = p[t].y;
-        r[(4 * g + 2) * 17 + c] = p[t].z;
-        r[(4 * g + 3) * 17 + c] = p[t].w;
+            for (int r = 0; r < R; ++r)
+                if (4 * g + r < mrows)
+                    yo[r * (size_t)N] = o[16 * r];
+        }
     }
-    __syncthreads();
-
-    // the Wc subtree roots -> the output; the whole workgroup shares the work
-    for (int o = tid; o < T * 256; o += blockDim.x) {
-        const int t = o >> 8;
-        const int row = (o >> 4) & 15;
-        const int col = o & 15;
-        const int n = (tile0 + t) * 16 + col;
-        if (row >= mrows || n >= N)
-            continue;
-        float v[16];
+    if constexpr (SPLIT) {
+        const int W = blockDim.x >> 6;
+        float *rw = red + wave * 16 * 17;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            v[j] = j < Wc ? red_lds[((j * T + t) * 16 + row) * 17 + col] : 0.f;
-        y[(size_t)(m0 + row) * N + n] = tree_sum<16>(v, Wc) * 16.0f;
+        for (int r = 0; r < R; ++r)
+            rw[(4 * g + r) * 17 + c] = root[r];
+        __syncthreads();
+        for (int o = threadIdx.x; o < 256; o += blockDim.x) {  // W may be below 4
+            const int row = o >> 4, col = o & 15;
+            const int n = 16 * t0 + col;
+            if (row < mrows && n < N) {
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    v[j] = j < W ? red[(j * 16 + row) * 17 + col] : 0.f;
+                y[(size_t)(m0 + row) * N + n] = tree_sum<16>(v, W);
+            }
+        }
     }
 }
 
@@ -280,8 +383,9 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
     const int st_q = tid & 3;
     const uint16_t *xsrc_row = x + (size_t)min(m0 + st_r, M - 1) * K;
 
+    const Dequant<BF16> dq;
     f32x4 p[2][2];
-    f32x4 stack[4][4];  // tree_push works on the four tiles as one array
+    TreeStack<4, f32x4> stack;  // the four tiles as one array
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -302,10 +406,10 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
                 const u32x4 *xsrc = (const u32x4 *)(xsrc_row + (size_t)bq * 32);
                 const u32x4 x0 = xsrc[0], x1 = xsrc[1], x2 = xsrc[2], x3 = xsrc[3];
                 const int col = 16 * wave + c;
-                *(u32x4 *)&ws[col][0 * 32 + 8 * g] = dequant8<BF16>(wv.x);
-                *(u32x4 *)&ws[col][1 * 32 + 8 * g] = dequant8<BF16>(wv.y);
-                *(u32x4 *)&ws[col][2 * 32 + 8 * g] = dequant8<BF16>(wv.z);
-                *(u32x4 *)&ws[col][3 * 32 + 8 * g] = dequant8<BF16>(wv.w);
+                *(u32x4 *)&ws[col][0 * 32 + 8 * g] = dq(wv.x);
+                *(u32x4 *)&ws[col][1 * 32 + 8 * g] = dq(wv.y);
+                *(u32x4 *)&ws[col][2 * 32 + 8 * g] = dq(wv.z);
+                *(u32x4 *)&ws[col][3 * 32 + 8 * g] = dq(wv.w);
                 if (g == 0) {
                     ds[0][col] = half_bits_to_float(sv.x & 0xFFFFu);
                     ds[1][col] = half_bits_to_float(sv.x >> 16);
@@ -325,6 +429,7 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
                 if (i < nq) {
                     u32x4 a[2], b[2];
                     float dsc[2];
+                    f32x4 E[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         a[t] = *(const u32x4 *)&xs[32 * wr + 16 * t + c][i * 32 + 8 * g];
@@ -333,16 +438,19 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
                     }
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
+                        E[rt] = blockdot<BF16>(a[rt], dq.offset);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                         for (int ct = 0; ct < 2; ++ct)
-                            scale_accumulate(p[rt][ct], dsc[ct], blockdot<BF16>(a[rt], b[ct]));
+                            scale_accumulate(p[rt][ct], dsc[ct], blockdot<BF16>(a[rt], b[ct]), E[rt]);
                 }
             }
             __syncthreads();
         }
         // ---- segment done: fold into the K-group's subtree
         f32x4 cur[4] = {p[0][0], p[0][1], p[1][0], p[1][1]};
-        if (!tree_push<4, 4>(stack, cur, li, L)) {
+        if (!stack.push(cur, li, L)) {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -356,7 +464,7 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
         }
     }
 
-    // ---- write: y = 16 * root, or the unscaled subtree root to the workspace
+    // ---- write: y = root, or the subtree root to the workspace
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -373,7 +481,7 @@ __global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
                 if (write_partial)
                     out[((size_t)z * M + m) * N + n] = v;
                 else
-                    out[(size_t)m * N + n] = v * 16.0f;
+                    out[(size_t)m * N + n] = v;
             }
         }
 }
@@ -389,13 +497,14 @@ __global__ __launch_bounds__(256) void q4_tree_combine(const float *__restrict__
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         v[j] = j < Gk ? part[(size_t)j * MN + i] : 0.f;
-    y[i] = tree_sum<16>(v, Gk) * 16.0f;
+    y[i] = tree_sum<16>(v, Gk);
 }
 
 // =================================================================== pack
-// One thread per (tile, quad, lane l = 16 g + c): gathers the 16 bytes of
-// lane l (bytes 4g..4g+3 of blocks 4q..4q+3 of column 16t + c, packed from
-// the canonical codes) and, for g == 0, the column's four scales.
+// One thread per (tile, quad, lane l = 16 g + c): gathers the four words of
+// lane l (codes of k = 32 b + 8 g + r, blocks b = 4q..4q+3 of column
+// 16t + c, code r at bit 4 (r / 2) + 16 (r % 2)) and, for g == 0, the
+// column's four scales.
 __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales_in,
                                                       uint8_t *__restrict__ wq,
@@ -421,11 +530,8 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict_
         if (n < N && b < nb) {
             const uint8_t *src = codes + (size_t)n * K + 32 * b + 8 * g;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = src[2 * j] & 0x0Fu;
-                const uint32_t hi = src[2 * j + 1] & 0x0Fu;
-                v |= (lo | (hi << 4)) << (8 * j);
-            }
+            for (int r = 0; r < 8; ++r)
+                v |= (uint32_t)(src[r] & 0x0Fu) << (4 * (r / 2) + 16 * (r % 2));
         }
         out[i] = v;
     }
@@ -445,40 +551,74 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict_
 }
 
 // ============================================================== launchers
-// Launch shape of the GEMV: column tiles per workgroup (T), waves per
-// workgroup (Wc: a power of two with S / Wc <= 4) and ring depth (D).  None
-// of them changes the bits.  Q4_GEMV_T, Q4_GEMV_WAVES and Q4_GEMV_DEPTH
+// Launch shape of the GEMV; none of it changes the bits.  Wide N: one
+// stream per wave over all of K, `tps` tiles per stream.  Narrow N: one
+// workgroup per column tile, W = S / L waves over runs of L segments.
+// Q4_GEMV_SPLIT (0/1), Q4_GEMV_RUN (L), Q4_GEMV_TPS and Q4_GEMV_DEPTH (4/8)
 // override the heuristic (tuning only).
-static int env_knob(const char *name)
+static int env_knob(const char *name, int dflt)
 {
     const char *v = getenv(name);
-    return v ? atoi(v) : 0;
+    return v ? atoi(v) : dflt;
 }
 
-// L (segments per wave) is 4 or 1: Wc = S / 4 or S.
-static void gemv_shape(int M, int N, const Plan &plan, int &T, int &L, int &D)
+struct GemvShape {
+    bool split, xl;
+    int L, tps, D;
+    size_t lds;  // dynamic LDS bytes
+};
+
+// x is staged in LDS when the rows (and the tile roots) fit in this budget
+// (bytes of dynamic LDS per workgroup).
+constexpr size_t GEMV_XLDS_MAX = 64 * 1024;
+
+static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
 {
-    (void)M;
-    // measured on MI355X (7B shapes): wide N streams two tiles per wave in runs
-    // of 4 segments; narrow N spreads one segment per wave over more waves
+    GemvShape sh;
     const int tiles = (N + 15) / 16;
-    const bool wide = plan.S >= 4 && tiles >= 1024;
-    T = wide ? 2 : 1;
-    D = 2;
-    L = wide ? 4 : 1;
-    static const int env_t = env_knob("Q4_GEMV_T");
-    static const int env_l = env_knob("Q4_GEMV_RUN");
-    static const int env_d = env_knob("Q4_GEMV_DEPTH");
-    if (env_t == 1 || env_t == 2)
-        T = env_t;
-    if (env_d == 2 || env_d == 3)
-        D = env_d;
-    if (env_l == 1 || (env_l == 4 && plan.S >= 4))
-        L = env_l;
+    sh.split = tiles < 1024;
+    // split: runs of about 4 quads, at most 8 waves
+    int L = 1;
+    while (L < plan.S && ((2 * L * plan.G) >> plan.log2S) <= 4)
+        L *= 2;
+    while (plan.S / L > 8)
+        L *= 2;
+    sh.L = L;
+    sh.tps = (tiles + 2047) / 2048;  // about 2048 streams
+    sh.D = 8;
+    static const int e_split = env_knob("Q4_GEMV_SPLIT", -1);
+    static const int e_run = env_knob("Q4_GEMV_RUN", 0);
+    static const int e_tps = env_knob("Q4_GEMV_TPS", 0);
+    static const int e_d = env_knob("Q4_GEMV_DEPTH", 0);
+    static const int e_xl = env_knob("Q4_GEMV_XLDS", -1);
+    if (e_split == 0 || e_split == 1)
+        sh.split = e_split == 1;
+    if (e_run > 0 && (e_run & (e_run - 1)) == 0 && e_run <= plan.S && plan.S / e_run <= 8)
+        sh.L = e_run;
+    if (e_tps > 0)
+        sh.tps = e_tps;
+    sh.tps = sh.tps < GEMV_TPS_MAX ? sh.tps : GEMV_TPS_MAX;
+    if (e_d == 4 || e_d == 8)
+        sh.D = e_d;
+    if (!sh.split)
+        sh.L = plan.S;  // one run of all S segments
+    // a stream's byte offsets stay below 2^31
+    const long long tile_bytes = (long long)plan.G * 1024;
+    while (sh.tps > 1 && sh.tps * tile_bytes >= (1LL << 31))
+        --sh.tps;
+    const size_t rows = (size_t)(M < 16 ? M : 16);
+    const size_t xbytes = rows * gemv_xrow_bytes(K) + 256;
+    const size_t roots = sh.split ? 0 : (size_t)4 * sh.tps * 256 * sizeof(float);
+    const bool fits = roots + xbytes <= GEMV_XLDS_MAX;
+    sh.xl = fits;
+    if (e_xl == 0 || e_xl == 1)
+        sh.xl = e_xl == 1 && fits;
+    if (!sh.xl && sh.split)
+        sh.D = 4;  // x rides in the ring: 22 registers a stage
+    sh.lds = roots + (sh.xl ? xbytes : 0);
+    return sh;
 }
 
-// Every compile-time variant the launcher can pick: BF16 x T {1,2} x D
-// {2,3} x R {1,2,4} x L {1,4} x SHORT.
 struct GemvArgs {
     dim3 grid, block;
     size_t lds;
@@ -487,62 +627,67 @@ struct GemvArgs {
     const uint8_t *wq;
     const uint16_t *scales;
     float *y;
-    int M, N, K;
+    int M, N, K, L, tps;
     Plan plan;
 };
 
-template <bool BF16, int T, int D, int R, int L>
+template <bool BF16, int R, int D, bool SPLIT, bool XL>
 static void launch_gemv_v(const GemvArgs &a)
 {
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv<BF16, T, D, R, L, true>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
+                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv<BF16, T, D, R, L, false>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
+                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
 }
 
-template <bool BF16, int T, int D, int R>
-static void launch_gemv_l(int L, const GemvArgs &a)
+// Built variants: x in LDS with an 8-deep ring; x in the ring with a 4-deep
+// (split) or 4/8-deep (one stream per wave) ring.
+template <bool BF16, int R>
+static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
 {
-    if (L == 4)
-        launch_gemv_v<BF16, T, D, R, 4>(a);
-    else
-        launch_gemv_v<BF16, T, D, R, 1>(a);
+    if (sh.xl) {
+        if (sh.split)
+            launch_gemv_v<BF16, R, 8, true, true>(a);
+        else
+            launch_gemv_v<BF16, R, 8, false, true>(a);
+    } else if (sh.split) {
+        launch_gemv_v<BF16, R, 4, true, false>(a);
+    } else if (sh.D == 4) {
+        launch_gemv_v<BF16, R, 4, false, false>(a);
+    } else {
+        launch_gemv_v<BF16, R, 8, false, false>(a);
+    }
 }
 
-template <bool BF16, int T, int D>
-static void launch_gemv_r(int R, int L, const GemvArgs &a)
+template <bool BF16>
+static void launch_gemv_b(int R, const GemvShape &sh, const GemvArgs &a)
 {
     if (R == 1)
-        launch_gemv_l<BF16, T, D, 1>(L, a);
+        launch_gemv_r<BF16, 1>(sh, a);
     else if (R == 2)
-        launch_gemv_l<BF16, T, D, 2>(L, a);
+        launch_gemv_r<BF16, 2>(sh, a);
     else
-        launch_gemv_l<BF16, T, D, 4>(L, a);
-}
-
-template <bool BF16, int T>
-static void launch_gemv_d(int D, int R, int L, const GemvArgs &a)
-{
-    // two tiles per wave with a 3-deep ring would spill registers: not built
-    if (T == 1 && D == 3)
-        launch_gemv_r<BF16, T, T == 1 ? 3 : 2>(R, L, a);
-    else
-        launch_gemv_r<BF16, T, 2>(R, L, a);
+        launch_gemv_r<BF16, 4>(sh, a);
 }
 
 hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
                        float *y, int M, int N, int K, hipStream_t stream)
 {
     const Plan plan = make_plan(K);
-    int T, L, D;
-    gemv_shape(M, N, plan, T, L, D);
-    const int Wc = plan.S / L;
+    const GemvShape sh = gemv_shape(M, N, plan, K);
+    const int tiles = (N + 15) / 16;
     GemvArgs a;
-    a.grid = dim3((N + 16 * T - 1) / (16 * T), (M + 15) / 16);
-    a.block = dim3(64 * Wc);
-    a.lds = (size_t)Wc * T * 16 * 17 * sizeof(float);
+    if (sh.split) {
+        a.grid = dim3(tiles, (M + 15) / 16);
+        a.block = dim3(64 * (plan.S / sh.L));
+    } else {
+        const int streams = (tiles + sh.tps - 1) / sh.tps;
+        a.grid = dim3((streams + 3) / 4, (M + 15) / 16);
+        a.block = dim3(256);
+    }
+    a.lds = sh.lds;
     a.stream = stream;
     a.x = (const uint16_t *)x;
     a.wq = wq;
@@ -551,20 +696,15 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     a.M = M;
     a.N = N;
     a.K = K;
+    a.L = sh.L;
+    a.tps = sh.tps;
     a.plan = plan;
     // every 16-row slice but a last short one has 16 rows; 3 rows use R = 4
     const int R = M >= 3 ? 4 : M;
-    if (bf16) {
-        if (T == 2)
-            launch_gemv_d<true, 2>(D, R, L, a);
-        else
-            launch_gemv_d<true, 1>(D, R, L, a);
-    } else {
-        if (T == 2)
-            launch_gemv_d<false, 2>(D, R, L, a);
-        else
-            launch_gemv_d<false, 1>(D, R, L, a);
-    }
+    if (bf16)
+        launch_gemv_b<true>(R, sh, a);
+    else
+        launch_gemv_b<false>(R, sh, a);
     return hipGetLastError();
 }
 

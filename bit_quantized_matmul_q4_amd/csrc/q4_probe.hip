@@ -4,8 +4,8 @@
 // data so the tests can check, on the hardware, the assumptions the fixed
 // reduction order rests on: the MFMA operand / result lane layout, that an
 // MFMA result element depends only on its own A row and B column (not on its
-// slot or on other rows), run-to-run determinism, and the exactness of the
-// nibble dequantization.  Not part of the product library.
+// slot or on other rows), run-to-run determinism, the nibble dequantization
+// and the corrected block dot.  Not part of the product library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,7 +26,19 @@ __global__ __launch_bounds__(256) void probe_dequant(const uint32_t *w, q4::u32x
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n)
-        out[i] = q4::dequant8<BF16>(w[i]);
+        out[i] = q4::Dequant<BF16>()(w[i]);
+}
+
+// The block dot of the order as the kernels run it: for lane data a (A
+// operand) and one packed code word w per lane, D = MFMA(a, dequant(w)) and
+// E = MFMA(a, V + 8); both are returned, [waves][64][4] each.
+template <bool BF16>
+__global__ __launch_bounds__(64) void probe_q4dot(const q4::u32x4 *a, const uint32_t *w, q4::f32x4 *d,
+                                                  q4::f32x4 *e)
+{
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    d[i] = q4::blockdot<BF16>(a[i], q4::Dequant<BF16>()(w[i]));
+    e[i] = q4::blockdot<BF16>(a[i], q4::Dequant<BF16>().offset);
 }
 
 // fmaf(d, s, +0) on the VALU, for the single-rounding check of the scale step.
@@ -65,6 +77,19 @@ int q4probe_dequant(const void *w, void *out, int n, int bf16, void *stream)
     else
         hipLaunchKernelGGL(probe_dequant<false>, grid, dim3(256), 0, (hipStream_t)stream,
                            (const uint32_t *)w, (q4::u32x4 *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int q4probe_q4dot(const void *a, const void *w, void *d, void *e, int waves, int bf16, void *stream)
+{
+    if (!a || !w || !d || !e || waves < 1)
+        return -1;
+    if (bf16)
+        hipLaunchKernelGGL(probe_q4dot<true>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const uint32_t *)w, (q4::f32x4 *)d, (q4::f32x4 *)e);
+    else
+        hipLaunchKernelGGL(probe_q4dot<false>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const uint32_t *)w, (q4::f32x4 *)d, (q4::f32x4 *)e);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

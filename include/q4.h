@@ -25,13 +25,14 @@
  *   - packed form (what q4_pack writes and the compute calls read): tiles
  *     of 16 rows (t = n / 16, c = n % 16) by 4 blocks (quad q = b / 4,
  *     i = b % 4), tile order [ceil(N/16)][ceil(K/128)].
- *       Wq: 1024 bytes per tile.  With g, j in 0..3, the byte at
- *         16 * (16 g + c) + 4 i + j holds the codes of k = 32 b + 8 g + 2 j
- *         (bits 0..3) and k + 1 (bits 4..7) of row n, block b = 4 q + i.
+ *       Wq: 1024 bytes per tile.  With g in 0..3, the little-endian
+ *         32-bit word at byte 16 * (16 g + c) + 4 i holds the codes of
+ *         k = 32 b + 8 g + r, r = 0..7, of row n, block b = 4 q + i: code
+ *         r at bit 4 (r / 2) + 16 (r % 2) (even r in the low half-word).
  *       Wscales: 64 binary16 per tile; element 4 c + i is d[n][b].
  *     Entries past N rows or K/32 blocks are zero.  The layout makes each
  *     16-byte load of a 64-lane wave contiguous and gives every lane the
- *     exact matrix-core operand words it needs.
+ *     codes of its matrix-core operand words, two k per mask-and-or.
  * Activations x: [M][K] row-major, bfloat16 (q4_linear) or binary16
  * (q4_linear_f16).  Output y: float32 [M][N] row-major, overwritten (no
  * bias, no accumulation into y).
@@ -57,12 +58,12 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 
 enum q4_status {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,      /* a required pointer is NULL */
-    Q4_ERR_SHAPE = -2,     /* M < 1, N < 1, K < 32, K % 32 != 0, or a size overflows */
+    Q4_ERR_SHAPE = -2,     /* M < 1, N < 1, K < 32, K % 32 != 0, K > 2^25, or a size overflows */
     Q4_ERR_ALIGN = -3,     /* x or Wq not 16-byte aligned, packed scales not 8-byte
                               aligned, y not 4-byte aligned (see each call) */
     Q4_ERR_ENUM = -4,      /* unknown dtype or kernel selector */

@@ -83,6 +83,7 @@ class Probe:
         self.lib.q4probe_mfma.argtypes = [vp, vp, vp, i, i, vp]
         self.lib.q4probe_dequant.argtypes = [vp, vp, i, i, vp]
         self.lib.q4probe_fma0.argtypes = [vp, vp, vp, i, vp]
+        self.lib.q4probe_q4dot.argtypes = [vp, vp, vp, vp, i, i, vp]
 
     def mfma(self, a_lanes: np.ndarray, b_lanes: np.ndarray, bf16: bool) -> np.ndarray:
         """a_lanes, b_lanes: uint16 [waves, 64, 8] -> float32 [waves, 64, 4]."""
@@ -106,6 +107,20 @@ class Probe:
         assert rc == 0
         torch.cuda.synchronize()
         return out.cpu().numpy().view(np.uint16).reshape(n, 8)
+
+    def q4dot(self, a_lanes: np.ndarray, words: np.ndarray, bf16: bool):
+        """a_lanes uint16 [waves, 64, 8], words uint32 [waves, 64] -> (D, E)
+        float32 [waves, 64, 4] each: the block dot and its correction."""
+        waves = a_lanes.shape[0]
+        a = torch.from_numpy(np.ascontiguousarray(a_lanes, np.uint16).view(np.int16)).to(DEV)
+        w = torch.from_numpy(np.ascontiguousarray(words, np.uint32).view(np.int32)).to(DEV)
+        d = torch.empty((waves, 64, 4), dtype=torch.float32, device=DEV)
+        e = torch.empty((waves, 64, 4), dtype=torch.float32, device=DEV)
+        rc = self.lib.q4probe_q4dot(a.data_ptr(), w.data_ptr(), d.data_ptr(), e.data_ptr(), waves, int(bf16),
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        return d.cpu().numpy(), e.cpu().numpy()
 
     def fma0(self, d: np.ndarray, s: np.ndarray) -> np.ndarray:
         n = d.shape[0]

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_and_strerror(lib):
-    assert lib.q4_abi_version() == 2
+    assert lib.q4_abi_version() == 3
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
     assert lib.q4_strerror(-99) == b"unknown status"
@@ -124,7 +124,7 @@ def test_argument_checks(lib):
     assert call(lib, kern=3) == _lib.Q4_ERR_ENUM
     assert call(lib, kern=-1) == _lib.Q4_ERR_ENUM
     for M, N, K in ((0, 16, 64), (4, 0, 64), (4, 16, 0), (4, 16, 48), (4, 16, 16), (-1, 16, 64),
-                    (1 << 30, 1 << 30, 32)):
+                    (1 << 30, 1 << 30, 32), (1, 16, (1 << 25) + 32)):
         assert call(lib, M=M, N=N, K=K) == _lib.Q4_ERR_SHAPE, (M, N, K)
     assert call(lib, x=FAKE + 2) == _lib.Q4_ERR_ALIGN
     assert call(lib, w=FAKE + 8) == _lib.Q4_ERR_ALIGN

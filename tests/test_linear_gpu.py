@@ -80,8 +80,9 @@ def test_one_hot_readout_exact(kernel, bf16):
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 @pytest.mark.parametrize("K", [32, 3584, 18944])
 def test_exact_regime(kernel, K):
-    """Integer x in [-4, 4], scales 2^-1..2^-4: every block sum is an integer
-    and every partial a multiple of 2^-4 below 2^19, so all are exact."""
+    """Integer x in [-4, 4], scales 2^-1..2^-4: both block dots (D, E, below
+    2^15) and their difference are integers, and every partial is a multiple
+    of 2^-4 below 2^19, so all are exact."""
     gu.note("exact regime kernel=%s K=%d" % (kernel, K))
     rng = np.random.default_rng(22 + K)
     M, N = 6, 48

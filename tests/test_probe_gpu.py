@@ -6,8 +6,12 @@
   which is what lets a row's bits ignore M and the other rows;
 * run-to-run determinism;
 * exactness when every partial sum is representable;
-* the nibble dequantization gives (q - 8)/16 exactly for every code at
-  every position;
+* the nibble dequantization gives the operand V + q (V = 128 in bf16, 1024
+  in fp16) exactly for every code at every position of a packed word;
+* the corrected block dot: D = MFMA(x, V + q) is the plain MFMA of the
+  dequantized operand, E = MFMA(x, V + 8) is the same for every column,
+  D == E for a block of all-8 codes, and fl(D - E) is within the fp32
+  accumulation bound of the exact sum of x (q - 8);
 * fmaf(d, s, 0) is the single-rounded product (no flush of subnormals).
 """
 import numpy as np
@@ -29,6 +33,13 @@ def enc(v: np.ndarray, bf16: bool) -> np.ndarray:
     if bf16:
         return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return v.astype(np.float16).view(np.uint16)
+
+
+def dec(bits: np.ndarray, bf16: bool) -> np.ndarray:
+    b = np.asarray(bits, np.uint16)
+    if bf16:
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return b.view(np.float16).astype(np.float64)
 
 
 def to_lanes(A: np.ndarray, B: np.ndarray):
@@ -118,6 +129,10 @@ def test_mfma_slot_invariance_and_determinism(probe, bf16):
     assert np.all(D4[:, 1:, :] == 0)
 
 
+MAGIC = {True: 0x4300, False: 0x6400}  # V = 128 (bf16), 1024 (fp16)
+SHIFTS = (4 * (np.arange(8) // 2) + 16 * (np.arange(8) % 2)).astype(np.uint32)  # code r's bit
+
+
 @pytest.mark.parametrize("bf16", [True, False])
 def test_dequant_every_code_every_position(probe, bf16):
     gu.note("dequant bf16=%s" % bf16)
@@ -125,9 +140,44 @@ def test_dequant_every_code_every_position(probe, bf16):
     words = np.concatenate([np.arange(16, dtype=np.uint64) * 0x11111111,
                             rng.integers(0, 1 << 32, size=4096, dtype=np.uint64)]).astype(np.uint32)
     got = probe.dequant(words, bf16)
-    codes = (words[:, None] >> (4 * np.arange(8, dtype=np.uint32))[None, :]) & 0xF
-    expect = enc((codes.astype(np.float64) - 8.0) / 16.0, bf16)
+    codes = (words[:, None] >> SHIFTS[None, :]) & 0xF
+    base = 128.0 if bf16 else 1024.0
+    expect = enc(codes.astype(np.float64) + base, bf16)
     assert np.array_equal(got, expect)
+    assert np.array_equal(got, (MAGIC[bf16] | codes).astype(np.uint16))
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_corrected_block_dot(probe, bf16):
+    gu.note("corrected block dot bf16=%s" % bf16)
+    rng = np.random.default_rng(16)
+    w = 96
+    xv = rng.normal(0, 1, size=(w, 16, 32)) * np.exp(rng.normal(0, 1.5, size=(w, 16, 1)))
+    A = enc(xv, bf16)
+    q = rng.integers(0, 16, size=(w, 32, 16)).astype(np.uint32)
+    q[:16] = 8  # all-8 blocks
+    # lane l = 16 g + c: codes of column c, k = 8 g + r, packed into one word
+    l = np.arange(64)
+    ks = (8 * (l // 16))[:, None] + np.arange(8)[None, :]
+    lane_codes = q[:, ks, (l % 16)[:, None]]  # [w, 64, 8]
+    words = (lane_codes << SHIFTS).sum(axis=-1, dtype=np.uint32)
+    Bv = (MAGIC[bf16] | q).astype(np.uint16)
+    a4, b4 = to_lanes(A, Bv)
+    D, E = probe.q4dot(a4, words, bf16)
+    # D is the plain MFMA of the dequantized operand
+    assert np.array_equal(D.view(np.uint32), probe.mfma(a4, b4, bf16).view(np.uint32))
+    Dm, Em = from_lanes(D), from_lanes(E)
+    # E depends on the row only
+    assert np.array_equal(Em.view(np.uint32), np.repeat(Em[:, :, :1], 16, axis=2).view(np.uint32))
+    # a block of all-8 codes: D == E, so the block dot is exactly zero
+    assert np.array_equal(Dm[:16].view(np.uint32), Em[:16].view(np.uint32))
+    # fl(D - E) against the exact sum, within the fp32 bound for D and E
+    xd = dec(A, bf16)
+    s = (Dm - Em).astype(np.float32).astype(np.float64)
+    exact = np.einsum("wmk,wkn->wmn", xd, q.astype(np.float64) - 8.0)
+    V = 128.0 if bf16 else 1024.0
+    bound = 2 * 33 * 2.0 ** -24 * (V + 15.0) * np.abs(xd).sum(axis=2)[:, :, None]
+    assert np.all(np.abs(s - exact) <= bound)
 
 
 def test_fma0_single_rounding(probe):
