@@ -137,9 +137,10 @@ __host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t
 //  SPLIT = false: block = 256; each wave streams `tps` consecutive column
 //    tiles over all of K (one run of S segments) and stores each tile's
 //    outputs itself.
-//  SPLIT = true: block = 64 W with W = S / L <= 8; workgroup = one column tile,
-//    wave w streams run w (segments w L .. w L + L - 1); the W run roots meet
-//    in LDS for the top of the pairwise tree.
+//  SPLIT = true: block = 64 TW W <= 512 with W = S / L; the workgroup owns TW
+//    column tiles, wave (slot, run) streams run `run` (segments run L ..
+//    run L + L - 1) of tile slot `slot`; each tile's W run roots meet in LDS
+//    for the top of the pairwise tree.
 //  XL: the workgroup first copies its x rows into LDS and every wave reads its
 //    A operands there; otherwise each stage loads them with the weights.
 //    Every wave of every workgroup reads the same few kilobytes of x, so as
@@ -171,11 +172,15 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     const int m0 = blockIdx.y * 16;
     const int mrows = min(16, M - m0);
 
+    // SPLIT: the workgroup's waves are TW tile slots by W runs (wave = slot W
+    // + run); W = S / L is a power of two
+    const int log2W = SPLIT ? plan.log2S - (31 - __builtin_clz(L)) : 0;
     int t0, ntiles, run;
     if constexpr (SPLIT) {
-        t0 = blockIdx.x;
-        ntiles = 1;
-        run = wave;
+        const int TW = (blockDim.x >> 6) >> log2W;
+        t0 = blockIdx.x * TW + (wave >> log2W);
+        ntiles = t0 < n16 ? 1 : 0;  // 0: a spare slot of the last workgroup
+        run = wave & ((1 << log2W) - 1);
     } else {
         t0 = (blockIdx.x * 4 + wave) * tps;
         ntiles = max(0, min(tps, n16 - t0));  // 0: a spare wave of the last workgroup
@@ -319,21 +324,22 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         }
     }
     if constexpr (SPLIT) {
-        const int W = blockDim.x >> 6;
+        const int W = 1 << log2W;
+        const int TW = (blockDim.x >> 6) >> log2W;
         float *rw = red + wave * 16 * 17;
 #pragma unroll
         for (int r = 0; r < R; ++r)
             rw[(4 * g + r) * 17 + c] = root[r];
         __syncthreads();
-        for (int o = threadIdx.x; o < 256; o += blockDim.x) {  // W may be below 4
-            const int row = o >> 4, col = o & 15;
-            const int n = 16 * t0 + col;
+        for (int o = threadIdx.x; o < TW * 256; o += blockDim.x) {
+            const int slot = o >> 8, row = (o >> 4) & 15, col = o & 15;
+            const int n = 16 * (blockIdx.x * TW + slot) + col;
             if (row < mrows && n < N) {
-                float v[16];
+                float v[8];
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    v[j] = j < W ? red[(j * 16 + row) * 17 + col] : 0.f;
-                y[(size_t)(m0 + row) * N + n] = tree_sum<16>(v, W);
+                for (int j = 0; j < 8; ++j)
+                    v[j] = j < W ? red[(((slot << log2W) + j) * 16 + row) * 17 + col] : 0.f;
+                y[(size_t)(m0 + row) * N + n] = tree_sum<8>(v, W);
             }
         }
     }
@@ -564,7 +570,7 @@ static int env_knob(const char *name, int dflt)
 
 struct GemvShape {
     bool split, xl;
-    int L, tps, D;
+    int L, tps, D, tw;  // tw: column tiles per split workgroup
     size_t lds;  // dynamic LDS bytes
 };
 
@@ -576,10 +582,13 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
 {
     GemvShape sh;
     const int tiles = (N + 15) / 16;
-    sh.split = tiles < 1024;
-    // split: runs of about 4 quads, at most 8 waves
+    // Measured on MI355X (7B shapes, M = 1..8): very wide N streams one tile
+    // per wave over all of K; otherwise a column tile is split over runs of
+    // segments, about 7 quads each (14 for wide N at one or two rows).
+    sh.split = tiles < 4096;
     int L = 1;
-    while (L < plan.S && ((2 * L * plan.G) >> plan.log2S) <= 4)
+    const int target = (tiles >= 1024 && M <= 2) ? 14 : 7;  // quads per run
+    while (L < plan.S && ((2 * L * plan.G) >> plan.log2S) <= target)
         L *= 2;
     while (plan.S / L > 8)
         L *= 2;
@@ -610,9 +619,15 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     const size_t xbytes = rows * gemv_xrow_bytes(K) + 256;
     const size_t roots = sh.split ? 0 : (size_t)4 * sh.tps * 256 * sizeof(float);
     const bool fits = roots + xbytes <= GEMV_XLDS_MAX;
-    sh.xl = fits;
+    // measured: staged x pays for up to 4 rows on wide or long-K matrices;
+    // beyond that its LDS footprint caps the waves a compute unit can hold
+    sh.xl = fits && M <= 4 && (tiles >= 1024 || K >= 8192);
     if (e_xl == 0 || e_xl == 1)
         sh.xl = e_xl == 1 && fits;
+    static const int e_tw = env_knob("Q4_GEMV_TW", 0);
+    sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
+    if (e_tw == 1 || e_tw == 2 || e_tw == 4)
+        sh.tw = sh.split && sh.xl && e_tw * (plan.S / sh.L) <= 8 ? e_tw : 1;
     if (!sh.xl && sh.split)
         sh.D = 4;  // x rides in the ring: 22 registers a stage
     sh.lds = roots + (sh.xl ? xbytes : 0);
@@ -680,8 +695,10 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     const int tiles = (N + 15) / 16;
     GemvArgs a;
     if (sh.split) {
-        a.grid = dim3(tiles, (M + 15) / 16);
-        a.block = dim3(64 * (plan.S / sh.L));
+        const int W = plan.S / sh.L;
+        const int TW = sh.tw;
+        a.grid = dim3((tiles + TW - 1) / TW, (M + 15) / 16);
+        a.block = dim3(64 * W * TW);
     } else {
         const int streams = (tiles + sh.tps - 1) / sh.tps;
         a.grid = dim3((streams + 3) / 4, (M + 15) / 16);
