@@ -35,6 +35,32 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q4_gemv_7b_layer_set_m1-8_traffic.md")
+KERNEL_SOURCES = ("bit_quantized_matmul_q4_amd/csrc/q4_kernels.hip", "bit_quantized_matmul_q4_amd/csrc/q4_device.hpp",
+                  "bit_quantized_matmul_q4_amd/csrc/q4_plan.hpp")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed byte-counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith("|"))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg: str) -> None:
     sys.stderr.write("[bench] %s\n" % msg)
     sys.stderr.flush()
@@ -51,6 +77,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--detail-json", default=None, help="also write the full results here")
+    ap.add_argument("--eager-step", action="store_true",
+                    help="run one step's launches eagerly (no graphs) and exit: for hardware-counter passes")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run 8 plain device copies of MIB MiB each and exit: calibrates byte counters")
     return ap.parse_args()
 
 
@@ -67,6 +97,17 @@ def main() -> int:
     import bit_quantized_matmul_q4_amd as q4
     import synth
     from bit_quantized_matmul_q4_amd import build as hip_build
+
+    if args.copy_calibration:
+        dev = torch.device("cuda:0")
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 8 copies of %d bytes (each reads and writes %d bytes)" % (n, n))
+        return 0
 
     if not os.path.exists(hip_build.LIB):
         hip_build.build_library()
@@ -121,6 +162,14 @@ def main() -> int:
 
     def step_bytes(M_list):
         return sum(synth.algorithmic_bytes(M, m.N, m.K) for M in M_list for m in mats)
+
+    if args.eager_step:
+        for M in Ms:
+            for mi in range(len(mats)):
+                call(mi, M, 0, args.kernel)
+        torch.cuda.synchronize()
+        log("eager step: %d launches, %d algorithmic bytes" % (len(Ms) * len(mats), step_bytes(Ms)))
+        return 0
 
     # ---- the step: 6 projections x M = 1..8, one graph per pool copy
     log("capturing %d step graphs" % P)
@@ -180,23 +229,28 @@ def main() -> int:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         os.environ.setdefault("OMP_NUM_THREADS", str(threads))
         oracle.load_library()
-        done_bytes, done_rows, t_cpu, sample = 0, 0, 0.0, []
+        done_bytes, done_rows, t_cpu, calls, passes = 0, 0, 0.0, 0, 0
         x_host = {K: xs[K][:8].view(torch.int16).cpu().numpy().view(np.uint16) for K in xs}
         w_host = [(base[mi].codes.cpu().numpy(), base[mi].scales.view(torch.int16).cpu().numpy().view(np.uint16))
                   for mi in range(len(mats))]
-        for M in Ms:
-            for mi, m in enumerate(mats):
-                if t_cpu > args.cpu_seconds:
-                    break
-                t0 = time.perf_counter()
-                oracle.linear_tiled(x_host[m.K][:M], True, w_host[mi][0], w_host[mi][1], m.N, m.K)
-                t_cpu += time.perf_counter() - t0
-                done_bytes += synth.algorithmic_bytes(M, m.N, m.K)
-                done_rows += M
-                sample.append("%s@M=%d" % (m.name, M))
+        # whole steps (the 48 calls in order) until the time budget is used;
+        # a step cut short by the budget still counts the calls it made
+        while t_cpu < args.cpu_seconds:
+            for M in Ms:
+                for mi, m in enumerate(mats):
+                    if t_cpu >= args.cpu_seconds and calls % len(mats) == 0:
+                        break
+                    t0 = time.perf_counter()
+                    oracle.linear_tiled(x_host[m.K][:M], True, w_host[mi][0], w_host[mi][1], m.N, m.K)
+                    t_cpu += time.perf_counter() - t0
+                    done_bytes += synth.algorithmic_bytes(M, m.N, m.K)
+                    done_rows += M
+                    calls += 1
+            passes += 1
         cpu = {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
-               "sample": "%d of the step's 48 calls (%s ... %s), %.1f s" % (len(sample), sample[0], sample[-1], t_cpu),
+               "sample": "%d calls of the step (%d pass(es) over its 48 calls, M = 1..8 x 6 matrices), %.1f s"
+                         % (calls, passes, t_cpu),
                "rows_per_s": round(done_rows / t_cpu, 2)}
         log("cpu oracle %.3f GB/s on %d threads" % (cpu["value"], threads))
 
@@ -219,7 +273,7 @@ def main() -> int:
                    "rotation_pool_copies": P, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 1),
                    "rows_per_s": round(rows_per_s, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "q4_gemv<bf16>", "launches_per_step": len(Ms) * len(mats),
                      "avg_bytes_per_launch": int(bytes_step / (len(Ms) * len(mats))),
                      "avg_launch_us": round(kern_ms / (len(Ms) * len(mats)) * 1e3, 3)},
