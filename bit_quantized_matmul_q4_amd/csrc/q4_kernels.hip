@@ -345,6 +345,156 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     }
 }
 
+// ============================================================ GEMV (seg)
+// The segment-stationary matrix-vector kernel, for S = 16 segments of at
+// most LQ quads (2048 <= K <= 6144).  A workgroup of 16 waves owns `tpw`
+// consecutive column tiles; wave j owns segment j of every one of them.  Its
+// A operands (x's blocks of segment j) and nothing else of x are loaded once
+// into registers, so the workgroup reads x exactly once; the wave then
+// streams its segment's tile-quads of all its tiles through a D-deep ring
+// (codes and scales only).  Per tile the segment partials go to LDS; every
+// TC tiles the workgroup meets at a barrier that does not wait for the ring
+// and runs the pairwise tree over the 16 partials; y is written at the end
+// (a store inside the streaming loop would make every ring wait drain).
+//
+// Ring positions are (tile i, quad q), q in [0, LQ); quads past the
+// segment's length are placeholders: their loads fall outside the
+// resources' ranges (zero, no memory access) and they compute nothing.
+// grid = (ceil(tiles / tpw), ceil(M / 16)), block = 1024.  With MR =
+// min(M, 16), dynamic LDS: roots [2][TC][16 seg][MR][16] floats, then
+// outputs [tpw][MR][16] floats.
+constexpr int SEG_TC = 2;  // tiles per combine
+
+__device__ __forceinline__ void workgroup_barrier_lds()
+{
+    // LDS writes done, then the barrier; outstanding global loads keep going
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool BF16, int R, int LQ, bool SHORT>
+__global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x,
+                                                    const uint8_t *__restrict__ wq,
+                                                    const uint16_t *__restrict__ scales,
+                                                    float *__restrict__ y, int M, int N, int K, Plan plan,
+                                                    int tpw)
+{
+    constexpr int D = 6;  // ring depth: a multiple of LQ
+    static_assert(D % LQ == 0, "ring positions must map to fixed quads");
+    constexpr int TC = SEG_TC;
+    extern __shared__ __attribute__((aligned(16))) float seg_lds[];
+    const int MR = min(M, 16);
+    float *roots = seg_lds;                        // [2][TC][16 seg][MR][16]
+    float *ystage = seg_lds + 2 * TC * 16 * MR * 16;  // [tpw][MR][16]
+
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // segment
+    const int g = lane >> 4, c = lane & 15;
+    const int n16 = (N + 15) / 16;
+    const int G = plan.G;
+    const int m0 = blockIdx.y * 16;
+    const int mrows = min(16, M - m0);
+    const int t_first = blockIdx.x * tpw;
+    const int ntiles = min(tpw, n16 - t_first);
+    const int qs = (j * G) >> 4;
+    const int len = (((j + 1) * G) >> 4) - qs;  // 1 .. LQ quads
+
+    // this segment's A operands, once
+    const uint32_t x_bytes = (uint32_t)mrows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
+    const uint32_t x_lane = (uint32_t)min(c, mrows - 1) * (uint32_t)K * 2u + 16u * g;
+    u32x4 xs[LQ][4];
+#pragma unroll
+    for (int q = 0; q < LQ; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            xs[q][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rx, x_lane + 64u * b, 256u * (qs + min(q, len - 1)), 0));
+
+    // the stream: tiles t_first .. t_first + ntiles - 1, quads qs .. qs + LQ - 1
+    const uint32_t tile_b = (uint32_t)G * 1024u, tile_s = (uint32_t)G * 128u;
+    const uint32_t w_range = (uint32_t)ntiles * tile_b, s_range = (uint32_t)ntiles * tile_s;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + (size_t)t_first * G * 1024, w_range);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + (size_t)t_first * G * 64, s_range);
+    const uint32_t w_lane = 16u * lane, s_lane = 8u * c;
+    const int npos = ntiles * LQ;
+
+    GemvStage ring[D];
+    // position -> (tile, quad); live unless the quad is past the segment or
+    // the tile past the workgroup's
+    auto load = [&](GemvStage &st, int pos, int q) {
+        const int i = pos / LQ;  // LQ is a compile-time constant
+        const bool live = q < len && pos < npos;
+        const uint32_t wo = live ? (uint32_t)i * tile_b + 1024u * (qs + q) : w_range;
+        const uint32_t so = live ? (uint32_t)i * tile_s + 128u * (qs + q) : s_range;
+        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, wo, 0));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane, so, 0));
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load(ring[d], d, d % LQ);
+        issue_fence();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): x and the prefill (see q4_gemv)
+
+    const Dequant<BF16> dq;
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        p[r] = 0.f;
+    for (int base = 0; base < npos; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int q = d % LQ;
+            const int pos = base + d;
+            const int i = pos / LQ;
+            if (pos < npos) {
+                if (q < len) {
+                    const int nq = SHORT && qs + q == G - 1 ? plan.nb - 4 * (G - 1) : 4;
+                    gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
+                }
+                if (q == LQ - 1) {  // the tile's segment partial is done
+                    float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (4 * g + r < mrows)
+                            rt[(4 * g + r) * 16 + c] = p[r];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        p[r] = 0.f;
+                    if (i % TC == TC - 1 || i == ntiles - 1) {  // chunk done: the tree
+                        workgroup_barrier_lds();
+                        const int i0 = i - i % TC;
+                        const float *rc = roots + ((i / TC) & 1) * TC * 16 * (MR * 16);
+                        for (int o = threadIdx.x; o < TC * 256; o += blockDim.x) {
+                            const int k = o >> 8, row = (o >> 4) & 15, col = o & 15;
+                            if (i0 + k <= i && row < mrows) {
+                                float v[16];
+#pragma unroll
+                                for (int sg = 0; sg < 16; ++sg)
+                                    v[sg] = rc[(k * 16 + sg) * (MR * 16) + row * 16 + col];
+                                ystage[((i0 + k) * MR + row) * 16 + col] = tree_sum<16>(v, 16);
+                            }
+                        }
+                    }
+                }
+            }
+            issue_fence();
+            load(ring[d], pos + D, q);  // refill D positions ahead (D % LQ == 0: same quad)
+            issue_fence();
+        }
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < ntiles * 256; o += blockDim.x) {
+        const int k = o >> 8, row = (o >> 4) & 15, col = o & 15;
+        const int n = 16 * (t_first + k) + col;
+        if (row < mrows && n < N)
+            y[(size_t)(m0 + row) * N + n] = ystage[(k * MR + row) * 16 + col];
+    }
+}
+
 // =================================================================== GEMM
 constexpr int GEMM_BM = 64;
 constexpr int GEMM_BN = 64;
@@ -687,10 +837,95 @@ static void launch_gemv_b(int R, const GemvShape &sh, const GemvArgs &a)
         launch_gemv_r<BF16, 4>(sh, a);
 }
 
+// ---- the segment-stationary form
+template <bool BF16, int R, int LQ>
+static void launch_seg_v(const GemvArgs &a)
+{
+    if (a.plan.nb & 3)
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true>), a.grid, a.block, a.lds, a.stream, a.x, a.wq, a.scales,
+                           a.y, a.M, a.N, a.K, a.plan, a.tps);
+    else
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false>), a.grid, a.block, a.lds, a.stream, a.x, a.wq, a.scales,
+                           a.y, a.M, a.N, a.K, a.plan, a.tps);
+}
+
+template <bool BF16, int R>
+static void launch_seg_r(int LQ, const GemvArgs &a)
+{
+    if (LQ == 1)
+        launch_seg_v<BF16, R, 1>(a);
+    else if (LQ == 2)
+        launch_seg_v<BF16, R, 2>(a);
+    else
+        launch_seg_v<BF16, R, 3>(a);
+}
+
+template <bool BF16>
+static void launch_seg_b(int R, int LQ, const GemvArgs &a)
+{
+    if (R == 1)
+        launch_seg_r<BF16, 1>(LQ, a);
+    else if (R == 2)
+        launch_seg_r<BF16, 2>(LQ, a);
+    else
+        launch_seg_r<BF16, 4>(LQ, a);
+}
+
+// The segment-stationary form applies with S = 16 segments of at most 3
+// quads, more than 256 column tiles and its LDS within 64 KB.  tpw: tiles
+// per workgroup, about one workgroup per compute unit.  Q4_GEMV_SEG=0 turns
+// it off, =2 lifts the tile-count rule (both for measurement).
+static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
+{
+    static const int e_seg = env_knob("Q4_GEMV_SEG", 1);
+    static const int e_tpw = env_knob("Q4_GEMV_SEG_TPW", 0);
+    if (!e_seg || plan.S != 16)
+        return false;
+    LQ = (plan.G + 15) / 16;
+    if (LQ > 3 || (LQ == 3 && M >= 3))  // 3-quad segments at 4 rows: 128 registers do not hold them
+        return false;
+    const int tiles = (N + 15) / 16;
+    // measured on MI355X: with one tile per workgroup or fewer (N <= 4096)
+    // the split form is faster
+    if (tiles <= 256 && e_seg != 2)
+        return false;
+    tpw = e_tpw > 0 ? e_tpw : (tiles + 255) / 256;
+    const int MR = M < 16 ? M : 16;
+    lds = (size_t)64 * MR * (2 * SEG_TC * 16 + tpw);
+    return lds <= GEMV_XLDS_MAX;
+}
+
 hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
                        float *y, int M, int N, int K, hipStream_t stream)
 {
     const Plan plan = make_plan(K);
+    const int R = M >= 3 ? 4 : M;
+    {
+        int LQ, tpw;
+        size_t lds;
+        if (seg_shape(M, N, plan, LQ, tpw, lds)) {
+            GemvArgs a;
+            a.grid = dim3(((N + 15) / 16 + tpw - 1) / tpw, (M + 15) / 16);
+            a.block = dim3(1024);
+            a.lds = lds;
+            a.stream = stream;
+            a.x = (const uint16_t *)x;
+            a.wq = wq;
+            a.scales = scales;
+            a.y = y;
+            a.M = M;
+            a.N = N;
+            a.K = K;
+            a.L = 1;
+            a.tps = tpw;
+            a.plan = plan;
+            if (bf16)
+                launch_seg_b<true>(R, LQ, a);
+            else
+                launch_seg_b<false>(R, LQ, a);
+            return hipGetLastError();
+        }
+    }
     const GemvShape sh = gemv_shape(M, N, plan, K);
     const int tiles = (N + 15) / 16;
     GemvArgs a;
@@ -717,7 +952,6 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     a.tps = sh.tps;
     a.plan = plan;
     // every 16-row slice but a last short one has 16 rows; 3 rows use R = 4
-    const int R = M >= 3 ? 4 : M;
     if (bf16)
         launch_gemv_b<true>(R, sh, a);
     else

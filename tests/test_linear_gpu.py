@@ -61,6 +61,25 @@ def test_parity_random(M, N, K, bf16, kernel):
     check(x, bf16, codes, s, kernel)
 
 
+# Wide N (more than 256 column tiles) with 2048 <= K <= 6144 takes the
+# matrix-vector kernel's segment-stationary form: segments of 1, 2 and 3
+# quads, a short last quad, ragged last tile and rows, 1..3 tiles per
+# workgroup with a partial last workgroup.
+SEG_SHAPES = [
+    (1, 4100, 2048, True), (2, 4112, 2080, False), (3, 4100, 3584, True), (2, 4100, 4128, True),
+    (9, 4100, 2048, False), (1, 8210, 2048, True), (8, 4352, 3584, True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,bf16", SEG_SHAPES)
+def test_segment_form_parity_and_bits(M, N, K, bf16):
+    gu.note("segment form M=%d N=%d K=%d bf16=%s" % (M, N, K, bf16))
+    x, codes, s = synth.problem(N, K, M, "bf16" if bf16 else "f16", workload=92, matrix=N * 7 + K)
+    y, _, _ = check(x, bf16, codes, s, "gemv")
+    y_mm = gu.run_linear(x, bf16, codes, s, kernel="gemm").cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y_mm.view(np.uint32))
+
+
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_one_hot_readout_exact(kernel, bf16):
