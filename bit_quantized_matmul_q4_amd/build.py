@@ -21,11 +21,13 @@ PROBE_LIB = os.path.join(HERE, "libq4probe.so")
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 
 # No fast-math, no FMA contraction (the reduction order uses explicit fmaf),
-# and no packed fp32 instructions.
+# and no packed fp32 instructions.  Matrix-core results go to ordinary vector
+# registers (the accumulator-register form costs a read-back per element).
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -142,12 +142,14 @@ __device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 D, f32
 // (left operand first), the first zero-bit the level cur then waits at.
 // After li = L-1, cur holds the run's subtree root and push() returns true;
 // otherwise cur must restart from +0.  The levels are separate named
-// registers written by value (selects), never through an index or a
-// pointer, so they cannot fall back to scratch memory.
+// registers written by value (selects or uniform branches), never through
+// an index or a pointer, so they cannot fall back to scratch memory.
 template <int NACC, typename T>
 struct TreeStack {
     T s0[NACC], s1[NACC], s2[NACC], s3[NACC];
 
+    // Per-element selects over every level: no branches (the form for
+    // frequent pushes of few values).
     __device__ __forceinline__ bool push(T (&cur)[NACC], int li, int L)
     {
         const bool m0 = li & 1, m1 = m0 && (li & 2), m2 = m1 && (li & 4), m3 = m2 && (li & 8);
@@ -170,6 +172,65 @@ struct TreeStack {
             s1[a] = w1 ? cur[a] : s1[a];
             s2[a] = w2 ? cur[a] : s2[a];
             s3[a] = w3 ? cur[a] : s3[a];
+        }
+        return root;
+    }
+
+    // Same result with real scalar branches: only the merging levels are
+    // added and one level is written (the form for many values per push).
+    __device__ __forceinline__ bool push_branch(T (&cur)[NACC], int li, int L)
+    {
+        // li is wave-uniform.  The empty volatile statements keep the
+        // compiler from turning the branches back into selects.
+        const int t = __builtin_amdgcn_readfirstlane(__builtin_ctz(~li));  // trailing one-bits
+        if (t > 0) {
+            asm volatile("");
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                cur[a] = s0[a] + cur[a];
+        }
+        if (t > 1) {
+            asm volatile("");
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                cur[a] = s1[a] + cur[a];
+        }
+        if (t > 2) {
+            asm volatile("");
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                cur[a] = s2[a] + cur[a];
+        }
+        if (t > 3) {
+            asm volatile("");
+#pragma unroll
+            for (int a = 0; a < NACC; ++a)
+                cur[a] = s3[a] + cur[a];
+        }
+        const bool root = li == L - 1;
+        if (!root) {
+            asm volatile("");
+            if (t == 0) {
+                asm volatile("");
+#pragma unroll
+                for (int a = 0; a < NACC; ++a)
+                    s0[a] = cur[a];
+            } else if (t == 1) {
+                asm volatile("");
+#pragma unroll
+                for (int a = 0; a < NACC; ++a)
+                    s1[a] = cur[a];
+            } else if (t == 2) {
+                asm volatile("");
+#pragma unroll
+                for (int a = 0; a < NACC; ++a)
+                    s2[a] = cur[a];
+            } else {
+                asm volatile("");
+#pragma unroll
+                for (int a = 0; a < NACC; ++a)
+                    s3[a] = cur[a];
+            }
         }
         return root;
     }

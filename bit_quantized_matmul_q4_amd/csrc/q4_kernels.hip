@@ -15,17 +15,26 @@
 //    the block dots on MFMA with all (<= 16) rows of x in the A operand.
 //    The runs' subtree roots meet in LDS for the top of the pairwise tree.
 //
-//  * q4_gemm: the LDS-staged tile kernel for larger M.  A workgroup owns a
-//    64 x 64 output tile; per quad it dequantizes the 64-column weight tile
-//    into LDS once and stages the 64 x 128 activation tile, and four waves
-//    run 2 x 2 MFMA tiles each from LDS.  K may be split across workgroups
-//    (one subtree of segments each) when a workspace is given;
-//    q4_tree_combine then joins the subtree roots in tree order.
+//  * q4_gemv_seg: the same kernel's form for wide N (more than 256 column
+//    tiles): a workgroup of 16 waves owns a run of column tiles, wave j
+//    owns segment j of all of them and holds that segment of x in
+//    registers, so the workgroup reads x once.
+//
+//  * q4_gemm_ring: the LDS-staged tile kernel for larger M.  A workgroup of
+//    eight waves owns a 64 x 128 output unit; per quad, the activation
+//    chunk, code tiles and scales stream into a ring in LDS by direct
+//    global-to-LDS loads, each wave dequantizes the code words of its two
+//    column tiles in registers and runs 2 x 2 MFMA tiles from LDS.  K may be
+//    split across workgroups (one subtree of segments each) when a
+//    workspace is given; q4_tree_combine then joins the subtree roots in
+//    tree order.
 //
 //  * q4_pack_kernel: canonical codes and scales -> the tiled layout.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <algorithm>
 
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
@@ -496,146 +505,202 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 }
 
 // =================================================================== GEMM
-constexpr int GEMM_BM = 64;
-constexpr int GEMM_BN = 64;
-constexpr int GEMM_LDK = 128 + 8;  // 16-bit elements per staged row (padded)
+// The streaming matrix-matrix kernel.  A workgroup of eight waves owns one
+// output unit of 64 rows by 128 columns (4 x 8 tiles of 16 x 16) and one
+// K-group; wave w computes the 2 x 2 tile block at row tiles 2 (w / 4), +1
+// and column tiles 2 (w % 4), +1.
+//
+// Per quad, the inputs arrive in a GL_DS-deep LDS ring by direct
+// global-to-LDS loads (no registers held in flight): the 64 x 128
+// activation chunk in A-operand order (lane l's 16 bytes at 16 l), the
+// unit's 8 code tiles and their scales.  Each wave reads its two column
+// tiles' code words and dequantizes them in registers (a column tile is
+// dequantized by the two waves that use it, which costs less than a round
+// trip of the operands through LDS); the correction dot E of a row tile
+// serves both column tiles.  One barrier per quad; segment partials fold
+// into the streaming pairwise tree in registers.
+//
+// Every wave issues the same number of ring loads per quad (out-of-range
+// ones return zeros without touching memory), so one immediate vmcnt means
+// "this quad has landed" for every wave.
+constexpr int GL_DS = 3;
+constexpr int GL_WAVES = 8;
+constexpr int GL_BM = 64, GL_CT = 8;
 
-// grid = (ceil(N/64), ceil(M/64), Gk), block = 256.  K-group z owns the
-// segments [z S/Gk, (z+1) S/Gk) -- a complete subtree of the pairwise tree.
+// s_waitcnt immediate: vmcnt <= n (n < 64), expcnt and lgkmcnt not waited.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+struct GlGeom {
+    static constexpr int RT = GL_BM / 16;               // row tiles per unit
+    static constexpr int XCH = RT * 4;                  // activation chunks (row tile, block)
+    static constexpr int XPW = XCH / GL_WAVES;          // ... per wave
+    static constexpr int XB = XCH * 1024;
+    static constexpr int CB = GL_CT * 1024;             // code tiles, one per wave
+    static constexpr int SB = 2 * GL_WAVES * 128;       // scales, two tile slots per wave
+    static constexpr int STAGE = XB + CB + SB;
+    static constexpr int LOADS = XPW + 2;               // ring loads per wave per quad
+    static constexpr int BYTES = GL_DS * STAGE;
+    static_assert(XCH % GL_WAVES == 0 && GL_CT == GL_WAVES, "even split over the waves");
+};
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void q4_gemm(const uint16_t *__restrict__ x,
-                                               const uint8_t *__restrict__ wq,
-                                               const uint16_t *__restrict__ scales,
-                                               float *__restrict__ out, int M, int N, int K,
-                                               Plan plan, int Gk, int write_partial)
+__global__ __launch_bounds__(512, 2) void q4_gemm_ring(const uint16_t *__restrict__ x,
+                                                       const uint8_t *__restrict__ wq,
+                                                       const uint16_t *__restrict__ scales,
+                                                       float *__restrict__ out, int M, int N, int K, Plan plan,
+                                                       int Gk, int write_partial)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[GEMM_BM][GEMM_LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[GEMM_BN][GEMM_LDK];
-    __shared__ float ds[4][GEMM_BN];
+    typedef GlGeom Ge;
+    typedef __attribute__((address_space(3))) void lds_t;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[Ge::BYTES];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wr = wave >> 1, wc = wave & 1;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = w >> 2, wc = w & 3;
     const int g = lane >> 4, c = lane & 15;
-    const int n0 = blockIdx.x * GEMM_BN;
-    const int m0 = blockIdx.y * GEMM_BM;
-    const int z = blockIdx.z;
+    const int m0 = blockIdx.y * GL_BM;
+    const int mrows = __builtin_amdgcn_readfirstlane(min(GL_BM, M - m0));
     const int G = plan.G;
     const int n16 = (N + 15) / 16;
+    const int tb = blockIdx.x * GL_CT;  // first column tile of the unit
+    const int nct = __builtin_amdgcn_readfirstlane(min(GL_CT, n16 - tb));
+    // K-group: segments [j0, j0 + L), quads [qbeg, qend)
+    const int L = plan.S / Gk;
+    const int j0 = blockIdx.z * L;
+    const int qbeg = (j0 * G) >> plan.log2S;
+    const int qend = ((j0 + L) * G) >> plan.log2S;
+    const int nquads = qend - qbeg;
 
-    const int L = plan.S / Gk;  // segments of this K-group (power of two)
-    const int j0 = z * L;
+    // ring load sources (resources in scalar registers: ranges via readfirstlane)
+    const uint32_t xrow = 2u * (uint32_t)K;
+    const uint32_t x_range = __builtin_amdgcn_readfirstlane(mrows * (int)xrow);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_range);
+    const uint32_t tile_b = (uint32_t)G * 1024u, tile_s = (uint32_t)G * 128u;
+    const uint32_t w_range = __builtin_amdgcn_readfirstlane(nct * (int)tile_b);
+    const uint32_t s_range = __builtin_amdgcn_readfirstlane(nct * (int)tile_s);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + (size_t)tb * G * 1024, w_range);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + (size_t)tb * G * 64, s_range);
 
-    // weight staging: wave u stages column tile n0/16 + u (clamped; columns
-    // past N carry unused data) -- lane (g, c) dequantizes its 16 bytes into
-    // columns 16u + c, k-slots 32i + 8g.., i = 0..3
-    const int wtile = min(n0 / 16 + wave, n16 - 1);
-    const uint8_t *wsrc = wq + (size_t)wtile * G * 1024 + 16 * lane;
-    const uint16_t *ssrc = scales + (size_t)wtile * G * 64 + 4 * c;
-    // activation staging: thread -> (row st_r, block-in-quad st_q); rows past
-    // M re-read row M-1 (never stored)
-    const int st_r = tid >> 2;
-    const int st_q = tid & 3;
-    const uint16_t *xsrc_row = x + (size_t)min(m0 + st_r, M - 1) * K;
+    // quad qq of the run into its ring stage (qq >= nquads: placeholders)
+    auto issue = [&](int qq) {
+        uint8_t *stg = ring + (qq % GL_DS) * Ge::STAGE;
+        const bool live = qq < nquads;
+        const int q = qbeg + qq;
+#pragma unroll
+        for (int h = 0; h < Ge::XPW; ++h) {
+            const int ch = w + GL_WAVES * h;  // chunk = rt * 4 + i
+            const int rt = ch >> 2, i = ch & 3;
+            const uint32_t off = live ? (uint32_t)(16 * rt + c) * xrow + 256u * q + 64u * i + 16u * g : x_range;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(stg + ch * 1024), 16, off, 0, 0, 0);
+        }
+        {
+            const int ct = w;
+            const uint32_t off = live && ct < nct ? (uint32_t)ct * tile_b + 1024u * q + 16u * lane : w_range;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_t *)(stg + Ge::XB + ct * 1024), 16, off, 0, 0, 0);
+        }
+        {
+            const int ct = 2 * w + (lane >> 5);
+            const uint32_t off = live && ct < nct ? (uint32_t)ct * tile_s + 128u * q + 4u * (lane & 31) : s_range;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(stg + Ge::XB + Ge::CB + w * 256), 4, off, 0, 0,
+                                                     0);
+        }
+    };
 
     const Dequant<BF16> dq;
-    f32x4 p[2][2];
-    TreeStack<4, f32x4> stack;  // the four tiles as one array
+    f32x4 p[4];  // [rt][ct] of the wave's 2 x 2 tiles
+    TreeStack<4, f32x4> stack;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            p[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; ++a)
+        p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    int li = 0;
+    int seg_end = ((j0 + 1) * G) >> plan.log2S;
+    const bool live_tiles = 32 * wr < mrows && 2 * wc < nct;  // wave-uniform
 
-    for (int li = 0; li < L; ++li) {
-        const int seg = j0 + li;
-        const int qb = (seg * G) >> plan.log2S;
-        const int qe = ((seg + 1) * G) >> plan.log2S;
-        for (int q = qb; q < qe; ++q) {
-            const int nq = min(4, plan.nb - 4 * q);
-            // ---- stage: dequantized weights, activations, scales
-            {
-                const u32x4 wv = *(const u32x4 *)(wsrc + (size_t)q * 1024);
-                const u32x2 sv = *(const u32x2 *)(ssrc + (size_t)q * 64);
-                const int bq = min(4 * q + st_q, plan.nb - 1);
-                const u32x4 *xsrc = (const u32x4 *)(xsrc_row + (size_t)bq * 32);
-                const u32x4 x0 = xsrc[0], x1 = xsrc[1], x2 = xsrc[2], x3 = xsrc[3];
-                const int col = 16 * wave + c;
-                *(u32x4 *)&ws[col][0 * 32 + 8 * g] = dq(wv.x);
-                *(u32x4 *)&ws[col][1 * 32 + 8 * g] = dq(wv.y);
-                *(u32x4 *)&ws[col][2 * 32 + 8 * g] = dq(wv.z);
-                *(u32x4 *)&ws[col][3 * 32 + 8 * g] = dq(wv.w);
-                if (g == 0) {
-                    ds[0][col] = half_bits_to_float(sv.x & 0xFFFFu);
-                    ds[1][col] = half_bits_to_float(sv.x >> 16);
-                    ds[2][col] = half_bits_to_float(sv.y & 0xFFFFu);
-                    ds[3][col] = half_bits_to_float(sv.y >> 16);
-                }
-                u32x4 *xdst = (u32x4 *)&xs[st_r][st_q * 32];
-                xdst[0] = x0;
-                xdst[1] = x1;
-                xdst[2] = x2;
-                xdst[3] = x3;
+#pragma unroll
+    for (int s = 0; s < GL_DS - 1; ++s)
+        issue(s);
+
+    for (int qq = 0; qq < nquads; ++qq) {
+        // quad qq landed (this wave's loads, in order; then everyone's), and
+        // every wave is done with quad qq - 1, whose stage the next loads take
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((GL_DS - 2) * Ge::LOADS));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(qq + GL_DS - 1);
+
+        const uint8_t *stg = ring + (qq % GL_DS) * Ge::STAGE;
+        const int q = qbeg + qq;
+        const int nq = min(4, plan.nb - 4 * q);
+        if (live_tiles) {
+            u32x4 cw[2];
+            u32x2 sw[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                cw[ct] = *(const u32x4 *)(stg + Ge::XB + (2 * wc + ct) * 1024 + 16 * lane);
+                sw[ct] = *(const u32x2 *)(stg + Ge::XB + Ge::CB + (2 * wc + ct) * 128 + 8 * c);
             }
-            __syncthreads();
-            // ---- compute: 2 x 2 MFMA tiles per wave per block
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (i < nq) {
-                    u32x4 a[2], b[2];
-                    float dsc[2];
-                    f32x4 E[2];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        a[t] = *(const u32x4 *)&xs[32 * wr + 16 * t + c][i * 32 + 8 * g];
-                        b[t] = *(const u32x4 *)&ws[32 * wc + 16 * t + c][i * 32 + 8 * g];
-                        dsc[t] = ds[i][32 * wc + 16 * t + c];
-                    }
+                    u32x4 A[2], B[2];
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
-                        E[rt] = blockdot<BF16>(a[rt], dq.offset);
+                        A[rt] = *(const u32x4 *)(stg + ((2 * wr + rt) * 4 + i) * 1024 + 16 * lane);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        B[ct] = dq(i == 0 ? cw[ct].x : i == 1 ? cw[ct].y : i == 2 ? cw[ct].z : cw[ct].w);
+                    // the six block dots first, so they overlap in the matrix pipe
+                    f32x4 E[2], Dm[4];
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        E[rt] = blockdot<BF16>(A[rt], dq.offset);
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                         for (int ct = 0; ct < 2; ++ct)
-                            scale_accumulate(p[rt][ct], dsc[ct], blockdot<BF16>(a[rt], b[ct]), E[rt]);
+                            Dm[2 * rt + ct] = blockdot<BF16>(A[rt], B[ct]);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) {
+                            const uint32_t sd = i < 2 ? sw[ct].x : sw[ct].y;
+                            const float d = half_bits_to_float((i & 1) ? sd >> 16 : sd & 0xFFFFu);
+                            scale_accumulate(p[2 * rt + ct], d, Dm[2 * rt + ct], E[rt]);
+                        }
                 }
             }
-            __syncthreads();
         }
-        // ---- segment done: fold into the K-group's subtree
-        f32x4 cur[4] = {p[0][0], p[0][1], p[1][0], p[1][1]};
-        if (!stack.push(cur, li, L)) {
+        if (q + 1 == seg_end) {  // segment j0 + li done
+            if (!stack.push_branch(p, li, L)) {
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    p[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        } else {
-            p[0][0] = cur[0];
-            p[0][1] = cur[1];
-            p[1][0] = cur[2];
-            p[1][1] = cur[3];
+                for (int a = 0; a < 4; ++a)
+                    p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+            ++li;
+            seg_end = ((j0 + li + 1) * G) >> plan.log2S;
         }
     }
+    // the placeholder loads land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // ---- write: y = root, or the subtree root to the workspace
+    // p holds the K-group's subtree roots
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            const int n = n0 + 32 * wc + 16 * ct + c;
+            const int n = 16 * (tb + 2 * wc + ct) + c;
             if (n >= N)
                 continue;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 32 * wr + 16 * rt + 4 * g + r;
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + 32 * wr + 16 * rt + 4 * g + e;
                 if (m >= M)
                     continue;
-                const float v = r == 0 ? p[rt][ct].x : r == 1 ? p[rt][ct].y : r == 2 ? p[rt][ct].z : p[rt][ct].w;
+                const f32x4 v4 = p[2 * rt + ct];
+                const float v = e == 0 ? v4.x : e == 1 ? v4.y : e == 2 ? v4.z : v4.w;
                 if (write_partial)
-                    out[((size_t)z * M + m) * N + n] = v;
+                    out[((size_t)blockIdx.z * M + m) * N + n] = v;
                 else
                     out[(size_t)m * N + n] = v;
             }
@@ -959,22 +1024,41 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     return hipGetLastError();
 }
 
-static int gemm_split(int M, int N, int K, size_t workspace_bytes)
+// Streaming matrix-matrix kernel shape: 64 x 128 units, K split over Gk
+// groups when a workspace allows and the grid would otherwise hold fewer
+// than about two units per compute unit.
+struct GemmShape {
+    int nx, ny, gk;
+};
+
+static constexpr int kComputeUnits = 256;
+
+static GemmShape gemm_shape(int M, int N, int K, size_t workspace_bytes)
 {
     const Plan plan = make_plan(K);
-    const long long tiles = (long long)((M + GEMM_BM - 1) / GEMM_BM) * ((N + GEMM_BN - 1) / GEMM_BN);
-    int gk = 1;
-    while (gk < plan.S && tiles * gk < 1024)
-        gk *= 2;
-    while (gk > 1 && (size_t)gk * M * N * sizeof(float) > workspace_bytes)
-        gk /= 2;
-    return gk;
+    GemmShape sh;
+    sh.ny = (M + GL_BM - 1) / GL_BM;
+    sh.nx = ((N + 15) / 16 + GL_CT - 1) / GL_CT;
+    sh.gk = 1;
+    while (sh.gk < plan.S && (long long)sh.nx * sh.ny * sh.gk < 2 * kComputeUnits &&
+           (size_t)(2 * sh.gk) * M * N * sizeof(float) <= workspace_bytes)
+        sh.gk *= 2;
+    return sh;
 }
 
 size_t gemm_workspace_bytes(int M, int N, int K)
 {
-    const int gk = gemm_split(M, N, K, (size_t)-1);
-    return gk > 1 ? (size_t)gk * M * N * sizeof(float) : 0;
+    const GemmShape sh = gemm_shape(M, N, K, (size_t)-1);
+    return sh.gk > 1 ? (size_t)sh.gk * M * N * sizeof(float) : 0;
+}
+
+template <bool BF16>
+static void launch_gemm_ring(const GemmShape &sh, const uint16_t *x, const uint8_t *wq, const uint16_t *scales,
+                             float *out, int M, int N, int K, const Plan &plan, hipStream_t stream)
+{
+    const dim3 grid(sh.nx, sh.ny, sh.gk);
+    hipLaunchKernelGGL((q4_gemm_ring<BF16>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K, plan, sh.gk,
+                       sh.gk > 1 ? 1 : 0);
 }
 
 hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
@@ -982,21 +1066,18 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
                        hipStream_t stream)
 {
     const Plan plan = make_plan(K);
-    const int gk = workspace ? gemm_split(M, N, K, workspace_bytes) : 1;
-    const dim3 grid((N + GEMM_BN - 1) / GEMM_BN, (M + GEMM_BM - 1) / GEMM_BM, gk);
-    float *out = gk > 1 ? (float *)workspace : y;
+    const GemmShape sh = gemm_shape(M, N, K, workspace ? workspace_bytes : 0);
+    float *out = sh.gk > 1 ? (float *)workspace : y;
     if (bf16)
-        hipLaunchKernelGGL(q4_gemm<true>, grid, dim3(256), 0, stream, (const uint16_t *)x, wq, scales,
-                           out, M, N, K, plan, gk, gk > 1 ? 1 : 0);
+        launch_gemm_ring<true>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
     else
-        hipLaunchKernelGGL(q4_gemm<false>, grid, dim3(256), 0, stream, (const uint16_t *)x, wq, scales,
-                           out, M, N, K, plan, gk, gk > 1 ? 1 : 0);
+        launch_gemm_ring<false>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || gk == 1)
+    if (e != hipSuccess || sh.gk == 1)
         return e;
     const size_t mn = (size_t)M * N;
     hipLaunchKernelGGL(q4_tree_combine, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
-                       (const float *)workspace, y, mn, gk);
+                       (const float *)workspace, y, mn, sh.gk);
     return hipGetLastError();
 }
 
