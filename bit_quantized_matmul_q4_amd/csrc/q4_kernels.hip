@@ -372,7 +372,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // grid = (ceil(tiles / tpw), ceil(M / 16)), block = 1024.  With MR =
 // min(M, 16), dynamic LDS: roots [2][TC][16 seg][MR][16] floats, then
 // outputs [tpw][MR][16] floats.
-constexpr int SEG_TC = 2;  // tiles per combine
+// TC: tiles per combine (2; 1 above 8 rows, where the partials take 4 KB a row)
+static inline int seg_tc(int M) { return M > 8 ? 1 : 2; }
 
 __device__ __forceinline__ void workgroup_barrier_lds()
 {
@@ -383,7 +384,7 @@ __device__ __forceinline__ void workgroup_barrier_lds()
     asm volatile("" ::: "memory");
 }
 
-template <bool BF16, int R, int LQ, bool SHORT>
+template <bool BF16, int R, int LQ, bool SHORT, int TC>
 __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x,
                                                     const uint8_t *__restrict__ wq,
                                                     const uint16_t *__restrict__ scales,
@@ -392,7 +393,6 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 {
     constexpr int D = 6;  // ring depth: a multiple of LQ
     static_assert(D % LQ == 0, "ring positions must map to fixed quads");
-    constexpr int TC = SEG_TC;
     extern __shared__ __attribute__((aligned(16))) float seg_lds[];
     const int MR = min(M, 16);
     float *roots = seg_lds;                        // [2][TC][16 seg][MR][16]
@@ -903,15 +903,38 @@ static void launch_gemv_b(int R, const GemvShape &sh, const GemvArgs &a)
 }
 
 // ---- the segment-stationary form
+// The segment-stationary form runs one 1024-thread workgroup per compute
+// unit, so it may take LDS beyond the default 64 KB dynamic limit.
+constexpr size_t SEG_LDS_MAX = 160 * 1024;
+
+template <bool BF16, int R, int LQ, int TC>
+static void launch_seg_t(const GemvArgs &a)
+{
+    static const bool lds_raised = [] {
+        // a failure here leaves the default limit; the launch then reports it
+        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, true, TC>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEG_LDS_MAX);
+        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, false, TC>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEG_LDS_MAX);
+        return true;
+    }();
+    (void)lds_raised;
+    if (a.plan.nb & 3)
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
+                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.tps);
+    else
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
+                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.tps);
+}
+
 template <bool BF16, int R, int LQ>
 static void launch_seg_v(const GemvArgs &a)
 {
-    if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true>), a.grid, a.block, a.lds, a.stream, a.x, a.wq, a.scales,
-                           a.y, a.M, a.N, a.K, a.plan, a.tps);
-    else
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false>), a.grid, a.block, a.lds, a.stream, a.x, a.wq, a.scales,
-                           a.y, a.M, a.N, a.K, a.plan, a.tps);
+    if constexpr (R == 4) {
+        if (seg_tc(a.M) == 1)
+            return launch_seg_t<BF16, R, LQ, 1>(a);
+    }
+    launch_seg_t<BF16, R, LQ, 2>(a);
 }
 
 template <bool BF16, int R>
@@ -937,7 +960,7 @@ static void launch_seg_b(int R, int LQ, const GemvArgs &a)
 }
 
 // The segment-stationary form applies with S = 16 segments of at most 3
-// quads, more than 256 column tiles and its LDS within 64 KB.  tpw: tiles
+// quads, more than 256 column tiles and its LDS within 160 KB.  tpw: tiles
 // per workgroup, about one workgroup per compute unit.  Q4_GEMV_SEG=0 turns
 // it off, =2 lifts the tile-count rule (both for measurement).
 static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
@@ -956,8 +979,8 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
         return false;
     tpw = e_tpw > 0 ? e_tpw : (tiles + 255) / 256;
     const int MR = M < 16 ? M : 16;
-    lds = (size_t)64 * MR * (2 * SEG_TC * 16 + tpw);
-    return lds <= GEMV_XLDS_MAX;
+    lds = (size_t)64 * MR * (2 * seg_tc(M) * 16 + tpw);
+    return lds <= SEG_LDS_MAX;
 }
 
 hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,

@@ -67,7 +67,8 @@ def test_parity_random(M, N, K, bf16, kernel):
 # workgroup with a partial last workgroup.
 SEG_SHAPES = [
     (1, 4100, 2048, True), (2, 4112, 2080, False), (3, 4100, 3584, True), (2, 4100, 4128, True),
-    (9, 4100, 2048, False), (1, 8210, 2048, True), (8, 4352, 3584, True),
+    (9, 4100, 2048, False), (1, 8210, 2048, True), (8, 4352, 3584, True), (16, 4112, 3584, True),
+    (13, 8210, 2080, False),
 ]
 
 
