@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--pool-gib", type=float, default=1.5, help="rotation pool of weight copies (GiB)")
     ap.add_argument("--no-crossover", action="store_true", help="skip the GEMV/GEMM crossover sweep")
+    ap.add_argument("--no-stream", action="store_true", help="skip the 28-layer decode weight stream")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-launch step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "gemm"])
@@ -120,13 +122,29 @@ def main() -> int:
     log("device %s, rotation pool %d copies of the layer set (%.2f GiB)"
         % (torch.cuda.get_device_name(dev), P, P * set_bytes / (1 << 30)))
 
-    # ---- inputs, resident in HBM: weights drawn directly in the packed form
+    # ---- inputs, resident in HBM: weights drawn directly in the packed form.
+    # Each copy of the set is held as the fused buffers (q|k|v, gate|up,
+    # down); the six projections are views into them.
     base = []
     for mi, m in enumerate(mats):
         wq_t, sc_t = synth.packed_weight(m.N, m.K, 3, mi)
         base.append(q4.Q4Weight(torch.from_numpy(wq_t).to(dev),
                                 torch.from_numpy(sc_t.view(np.int16)).to(dev).view(torch.float16), m.N, m.K))
-    pool = [[q4.Q4Weight(b.codes.clone(), b.scales.clone(), b.N, b.K) for b in base] for _ in range(P)]
+    fuse_groups = ((0, 1, 2), (3, 4), (5,))  # q|k|v, gate|up, down
+
+    def fused_copy():
+        fused = [q4.concat_n([base[i] for i in grp]) for grp in fuse_groups]
+        views = []
+        for f, grp in zip(fused, fuse_groups):
+            views += q4.split_n(f, [mats[i].N for i in grp])
+        return fused, views
+
+    fpool, pool = [], []
+    for _ in range(P):
+        f, v = fused_copy()
+        fpool.append(f)
+        pool.append(v)
+    fmats = [(sum(mats[i].N for i in grp), mats[grp[0]].K) for grp in fuse_groups]
     Mmax = 128
     xs = {}
     for K in sorted({m.K for m in mats}):
@@ -134,11 +152,17 @@ def main() -> int:
         xs[K] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
     ys = {(mi, M): torch.empty((M, m.N), dtype=torch.float32, device=dev)
           for mi, m in enumerate(mats) for M in range(1, Mmax + 1)
-          if M <= 16 or M in (20, 24, 32, 48, 64, 96, 124, 128)}
+          if M <= 16 or M in (20, 24, 28, 32, 36, 40, 44, 48, 64, 96, 124, 128)}
     torch.cuda.synchronize()
+
+    yf = {(j, M): torch.empty((M, fmats[j][0]), dtype=torch.float32, device=dev)
+          for j in range(len(fmats)) for M in (1, 2, 3, 4, 5, 6, 7, 8, 16, 64)}
 
     def call(mi, M, p, kernel):
         q4.linear(xs[mats[mi].K][:M], pool[p][mi], out=ys[(mi, M)], kernel=kernel)
+
+    def call_fused(j, M, w):
+        q4.linear(xs[fmats[j][1]][:M], w, out=yf[(j, M)])
 
     def capture(fn):
         # warm the launch path (and any workspace) once outside capture
@@ -203,10 +227,67 @@ def main() -> int:
     log("per-M GB/s %s" % per_m)
     log("per-matrix GB/s at M=8 %s" % per_matrix_m8)
 
+    # ---- the same step with fused launches: q|k|v (N = 4608) and gate|up
+    # (N = 37888) as one call each, down on its own (24 calls); x is read
+    # once per fused call, so the step's algorithmic bytes are a little lower
+    fused_step = None
+    if not args.no_fused:
+        fgraphs = [capture(lambda p=p: [call_fused(j, M, fpool[p][j]) for M in Ms for j in range(len(fmats))])
+                   for p in range(P)]
+        for i in range(args.warmup):
+            fgraphs[i % P].replay()
+        ms_fused = time_graphs(fgraphs, args.steps)
+        fbytes = sum(synth.algorithmic_bytes(M, N, K) for M in Ms for (N, K) in fmats)
+        fused_step = {"calls_per_step": len(Ms) * len(fmats), "us_per_step": round(ms_fused * 1e3, 2),
+                      "gbs": round(fbytes / (ms_fused * 1e-3) / 1e9, 1),
+                      "pct_of_peak": round(100 * fbytes / (ms_fused * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+                      "rows_per_s": round(sum(Ms) / (ms_fused * 1e-3), 1),
+                      "matrices": ["q|k|v %dx%d" % fmats[0], "gate|up %dx%d" % fmats[1], "down %dx%d" % fmats[2]]}
+        log("fused step %.2f us, %.1f GB/s" % (ms_fused * 1e3, fused_step["gbs"]))
+        del fgraphs
+
+    # ---- the whole 7B decode weight stream: 28 distinct copies of the layer
+    # set plus the LM head, per M, as one graph (unfused and fused calls)
+    stream = None
+    if not args.no_stream:
+        from synth import LM_HEAD_7B, N_LAYERS_7B
+        layers = [fused_copy() for _ in range(N_LAYERS_7B)]
+        wq_t, sc_t = synth.packed_weight(LM_HEAD_7B.N, LM_HEAD_7B.K, 5, 6)
+        head = q4.Q4Weight(torch.from_numpy(wq_t).to(dev),
+                           torch.from_numpy(sc_t.view(np.int16)).to(dev).view(torch.float16),
+                           LM_HEAD_7B.N, LM_HEAD_7B.K)
+        del wq_t, sc_t
+        stream = {}
+        for M in (1, 4, 16, 64):
+            yh = torch.empty((M, LM_HEAD_7B.N), dtype=torch.float32, device=dev)
+
+            def run(fused, M=M, yh=yh):
+                for f, v in layers:
+                    if fused:
+                        for j in range(len(fmats)):
+                            call_fused(j, M, f[j])
+                    else:
+                        for mi in range(len(mats)):
+                            q4.linear(xs[mats[mi].K][:M], v[mi], out=ys[(mi, M)])
+                q4.linear(xs[LM_HEAD_7B.K][:M], head, out=yh)
+            nbytes = N_LAYERS_7B * step_bytes([M]) + synth.algorithmic_bytes(M, LM_HEAD_7B.N, LM_HEAD_7B.K)
+            rec = {}
+            for fused in (False, True):
+                g = capture(lambda fused=fused: run(fused))
+                ms = time_graphs([g], 5)
+                del g
+                rec["fused" if fused else "unfused"] = {
+                    "us": round(ms * 1e3, 1), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "rows_per_s": round(M / (ms * 1e-3), 1)}
+            stream[str(M)] = rec
+            log("decode stream M=%d: %s" % (M, rec))
+        del layers, head
+        torch.cuda.empty_cache()
+
     # ---- GEMV -> GEMM crossover on the layer set
     crossover = None
     if not args.no_crossover:
-        cM = list(range(1, 17)) + [20, 24, 32, 48, 64, 96, 124, 128]
+        cM = list(range(1, 17)) + [20, 24, 28, 32, 36, 40, 44, 48, 64, 96, 124, 128]
         table = []
         for M in cM:
             t = {}
@@ -274,11 +355,12 @@ def main() -> int:
                    "rows_per_s": round(rows_per_s, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "q4_gemv<bf16>", "launches_per_step": len(Ms) * len(mats),
+                     "kernel": "q4_gemv (split and segment forms), bf16", "launches_per_step": len(Ms) * len(mats),
                      "avg_bytes_per_launch": int(bytes_step / (len(Ms) * len(mats))),
                      "avg_launch_us": round(kern_ms / (len(Ms) * len(mats)) * 1e3, 3)},
         "cpu_baseline": cpu,
-        "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "crossover": crossover},
+        "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "fused_step": fused_step,
+                   "decode_stream_7b": stream, "crossover": crossover},
     }
     line = json.dumps(out)
     if args.detail_json:

@@ -23,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import KERNELS, Q4Error
 
-__all__ = ["Q4Weight", "linear", "pack", "packed_sizes", "workspace_bytes", "get_crossover",
+__all__ = ["Q4Weight", "linear", "pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
            "set_crossover", "segments", "Q4Error", "library_path"]
 
 
@@ -154,3 +154,42 @@ def set_crossover(T: int) -> None:
 
 def segments(K: int) -> int:
     return int(_lib.load().q4_segments(int(K)))
+
+
+def concat_n(weights) -> Q4Weight:
+    """Packed weights of one K stacked along N, for fused launches (q|k|v,
+    gate|up): one call then computes all of them.  The packed form is
+    tile-major along N, so concatenating the packed buffers packs the
+    concatenated rows; every part but the last must have N a multiple of
+    16 (no padding rows inside).  Each output column keeps its bits: the
+    reduction order depends on K only."""
+    weights = list(weights)
+    if not weights:
+        raise ValueError("concat_n needs at least one weight")
+    K = weights[0].K
+    for i, w in enumerate(weights):
+        if not isinstance(w, Q4Weight):
+            raise TypeError("concat_n takes Q4Weight objects")
+        if w.K != K:
+            raise ValueError("all weights must share K (%d != %d)" % (w.K, K))
+        if i + 1 < len(weights) and w.N % 16:
+            raise ValueError("every part but the last needs N % 16 == 0 (part %d has N=%d)" % (i, w.N))
+    codes = torch.cat([w.codes for w in weights])
+    scales = torch.cat([w.scales for w in weights])
+    return Q4Weight(codes, scales, sum(w.N for w in weights), K)
+
+
+def split_n(w: Q4Weight, Ns) -> list:
+    """Views of a packed weight as consecutive row blocks of Ns[i] rows
+    (all but the last a multiple of 16; sum(Ns) == w.N): the inverse of
+    concat_n, sharing w's memory."""
+    Ns = [int(n) for n in Ns]
+    if sum(Ns) != w.N or any(n < 1 for n in Ns) or any(n % 16 for n in Ns[:-1]):
+        raise ValueError("row blocks %s do not split N=%d on 16-row tiles" % (Ns, w.N))
+    out, c0, s0 = [], 0, 0
+    for n in Ns:
+        cb, sb = packed_sizes(n, w.K)
+        out.append(Q4Weight(w.codes[c0:c0 + cb], w.scales[s0:s0 + sb // 2], n, w.K))
+        c0 += cb
+        s0 += sb // 2
+    return out

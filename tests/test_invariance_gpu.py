@@ -113,3 +113,25 @@ def test_n_sharding(prob):
                          16 * (t1 - t0), K)
         y = q4.linear(xd[:20], sl, kernel="gemv")
         assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:20, 16 * t0:16 * t1])
+
+
+def test_fused_n_concat(prob):
+    """Weights sharing K, concatenated along N (one fused launch, as for
+    q|k|v or gate|up), give every part's columns bit for bit; split_n views
+    of the fused buffers give each part back."""
+    x, xd, w, codes, s, ref = prob
+    parts = [(0, 48), (48, 80), (80, 117)]
+    ws = [gu.pack_dev(np.ascontiguousarray(codes[a:b]), np.ascontiguousarray(s[a:b])) for a, b in parts]
+    fused = q4.concat_n(ws)
+    assert fused.N == 117
+    for kernel in ("gemv", "gemm"):
+        gu.note("fused concat kernel=%s" % kernel)
+        y = q4.linear(xd[:20], fused, kernel=kernel)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:20, 0:117])
+    for (a, b), v in zip(parts, q4.split_n(fused, [48, 32, 37])):
+        y = q4.linear(xd[:20], v, kernel="gemv")
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref[:20, a:b])
+    with pytest.raises(ValueError):
+        q4.concat_n([ws[2], ws[0]])  # a part before the last with N % 16 != 0
+    with pytest.raises(ValueError):
+        q4.split_n(fused, [40, 77])
