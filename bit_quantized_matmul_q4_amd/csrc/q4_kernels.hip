@@ -791,7 +791,10 @@ struct GemvShape {
 
 // x is staged in LDS when the rows (and the tile roots) fit in this budget
 // (bytes of dynamic LDS per workgroup).
-constexpr size_t GEMV_XLDS_MAX = 64 * 1024;
+// Dynamic LDS of the split form: what its 8.5 KB of static LDS leaves of the
+// 160 KB of a compute unit, less 1 KB (the launcher raises the 64 KB
+// default).  Staged x for 4 rows of K = 18944 fits.
+constexpr size_t GEMV_XLDS_MAX = 160 * 1024 - 8 * 16 * 17 * 4 - 1024;
 
 static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
 {
@@ -864,6 +867,17 @@ struct GemvArgs {
 template <bool BF16, int R, int D, bool SPLIT, bool XL>
 static void launch_gemv_v(const GemvArgs &a)
 {
+    if constexpr (XL) {
+        static const bool lds_raised = [] {
+            // a failure here leaves the default limit; the launch then reports it
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
+            return true;
+        }();
+        (void)lds_raised;
+    }
     if (a.plan.nb & 3)
         hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
                            a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
