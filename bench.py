@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--detail-json", default=None, help="also write the full results here")
     ap.add_argument("--eager-step", action="store_true",
                     help="run one step's launches eagerly (no graphs) and exit: for hardware-counter passes")
+    ap.add_argument("--eager-m", default=None, metavar="M,M,...",
+                    help="row counts of the eager step (default 1..8), e.g. 124 with --kernel gemm")
+    ap.add_argument("--eager-reps", type=int, default=1, help="repeat the eager step (weights from the pool)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run 8 plain device copies of MIB MiB each and exit: calibrates byte counters")
     return ap.parse_args()
@@ -188,11 +191,15 @@ def main() -> int:
         return sum(synth.algorithmic_bytes(M, m.N, m.K) for M in M_list for m in mats)
 
     if args.eager_step:
-        for M in Ms:
-            for mi in range(len(mats)):
-                call(mi, M, 0, args.kernel)
+        eMs = [int(v) for v in args.eager_m.split(",")] if args.eager_m else Ms
+        for r in range(args.eager_reps):
+            for M in eMs:
+                for mi in range(len(mats)):
+                    call(mi, M, r % P, args.kernel)
         torch.cuda.synchronize()
-        log("eager step: %d launches, %d algorithmic bytes" % (len(Ms) * len(mats), step_bytes(Ms)))
+        flops = sum(2 * M * m.N * m.K for M in eMs for m in mats)
+        log("eager step x %d: %d launches each, %d algorithmic bytes, %d useful flops per step"
+            % (args.eager_reps, len(eMs) * len(mats), step_bytes(eMs), flops))
         return 0
 
     # ---- the step: 6 projections x M = 1..8, one graph per pool copy
