@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--no-crossover", action="store_true", help="skip the GEMV/GEMM crossover sweep")
     ap.add_argument("--no-stream", action="store_true", help="skip the 28-layer decode weight stream")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-launch step")
+    ap.add_argument("--no-schemes", action="store_true", help="skip the pages' switching schemes comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "gemm"])
@@ -155,7 +156,7 @@ def main() -> int:
         xs[K] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
     ys = {(mi, M): torch.empty((M, m.N), dtype=torch.float32, device=dev)
           for mi, m in enumerate(mats) for M in range(1, Mmax + 1)
-          if M <= 16 or M in (20, 24, 28, 32, 36, 40, 44, 48, 64, 96, 124, 128)}
+          if M <= 16 or M in (19, 20, 24, 28, 32, 36, 40, 44, 48, 64, 85, 96, 124, 128)}
     torch.cuda.synchronize()
 
     yf = {(j, M): torch.empty((M, fmats[j][0]), dtype=torch.float32, device=dev)
@@ -291,6 +292,49 @@ def main() -> int:
         del layers, head
         torch.cuda.empty_cache()
 
+    # ---- the pages' kernel-switching schemes as comparators, on the layer
+    # set at the pages' row counts: 1..5 (one row per request) and the
+    # continuous-batching iterations 8, 19, 44, 85 tokens and the 124-row
+    # mixed batch.  Schemes: this library's rule (M <= T: one multi-row
+    # matrix-vector call, else matrix-matrix); one row -> matrix-vector, more
+    # -> matrix-matrix; up to 4 rows -> one matrix-vector call per row
+    # (written straight into its row of y), more -> matrix-matrix; every row
+    # through the matrix-vector kernel.  All four must give the same bits.
+    schemes = None
+    if not args.no_schemes:
+        T = q4.get_crossover()
+
+        def scheme_calls(name, M, p):
+            for mi, m in enumerate(mats):
+                x, w, y = xs[m.K][:M], pool[p][mi], ys[(mi, M)]
+                if name == "library" or name == "all_gemv":
+                    kern = "gemv" if (name == "all_gemv" or M <= T) else "gemm"
+                    q4.linear(x, w, out=y, kernel=kern)
+                elif name == "one_row_gemv" or M > 4:
+                    q4.linear(x, w, out=y, kernel="gemv" if M == 1 else "gemm")
+                else:  # row by row
+                    for r in range(M):
+                        q4.linear(x[r:r + 1], w, out=y[r:r + 1], kernel="gemv")
+
+        names = ("library", "one_row_gemv", "row_by_row_le4", "all_gemv")
+        schemes = {"T": T, "rows": {}, "bits_identical": True}
+        for M in (1, 2, 3, 4, 5, 8, 19, 44, 85, 124):
+            rec, outs = {}, {}
+            for name in names:
+                g = capture(lambda name=name, M=M: [scheme_calls(name, M, p % P) for p in range(4)])
+                rec[name] = round(time_graphs([g], 3) / 4 * 1e3, 2)  # us per layer set
+                del g
+                scheme_calls(name, M, 0)
+                torch.cuda.synchronize()
+                outs[name] = [ys[(mi, M)].clone() for mi in range(len(mats))]
+            for name in names[1:]:
+                for a, b in zip(outs["library"], outs[name]):
+                    if not torch.equal(a.view(torch.int32), b.view(torch.int32)):
+                        schemes["bits_identical"] = False
+            schemes["rows"][str(M)] = rec
+            log("schemes M=%d: %s" % (M, rec))
+        del outs
+
     # ---- GEMV -> GEMM crossover on the layer set
     crossover = None
     if not args.no_crossover:
@@ -367,7 +411,7 @@ def main() -> int:
                      "avg_launch_us": round(kern_ms / (len(Ms) * len(mats)) * 1e3, 3)},
         "cpu_baseline": cpu,
         "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "fused_step": fused_step,
-                   "decode_stream_7b": stream, "crossover": crossover},
+                   "decode_stream_7b": stream, "switching_schemes": schemes, "crossover": crossover},
     }
     line = json.dumps(out)
     if args.detail_json:
