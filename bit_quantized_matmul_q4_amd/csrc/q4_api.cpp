@@ -22,9 +22,10 @@
 namespace {
 
 // Measured GEMV -> GEMM crossover on MI355X (rows); M <= T runs the GEMV.
-// On the Qwen2.5-7B-shaped layer set the matrix-matrix kernel first wins at
-// M = 48 (the sum of the six projections' times), so T = 47.
-constexpr int kDefaultCrossover = 47;
+// On the Qwen2.5-7B-shaped layer set (the sum of the six projections' times)
+// the matrix-matrix kernel first wins at M = 33, where the matrix-vector
+// kernel needs a third 16-row slice; at 32 it is still 3% slower.  T = 32.
+constexpr int kDefaultCrossover = 32;
 
 thread_local int g_last_hip = 0;
 

@@ -1080,6 +1080,10 @@ static GemmShape gemm_shape(int M, int N, int K, size_t workspace_bytes)
     while (sh.gk < plan.S && (long long)sh.nx * sh.ny * sh.gk < 2 * kComputeUnits &&
            (size_t)(2 * sh.gk) * M * N * sizeof(float) <= workspace_bytes)
         sh.gk *= 2;
+    static const int e_gk = env_knob("Q4_GEMM_GK", 0);  // for measurement: forced split (power of two)
+    if (e_gk > 0 && (e_gk & (e_gk - 1)) == 0 && e_gk <= plan.S &&
+        (e_gk == 1 || (size_t)e_gk * M * N * sizeof(float) <= workspace_bytes))
+        sh.gk = e_gk;
     return sh;
 }
 
