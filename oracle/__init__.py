@@ -77,6 +77,10 @@ def _declare(lib):
     lib.q4o_pack_tiled.restype = None
     lib.q4o_unpack_tiled.argtypes = [u8p, u16p, u8p, u16p, i64, i64]
     lib.q4o_unpack_tiled.restype = None
+    lib.q4o_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.q4o_f64_to_f16.restype = ctypes.c_uint16
+    lib.q4o_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, u8p, u16p, i64, i64]
+    lib.q4o_quantize.restype = ctypes.c_int
     return lib
 
 
@@ -259,3 +263,29 @@ def max_normalised_error(y_test: np.ndarray, y_ref: np.ndarray, a_ref: np.ndarra
         return float("inf")
     rel = np.where(zero, 0.0, diff / np.where(zero, 1.0, a_ref))
     return float(rel.max()) if rel.size else 0.0
+
+
+def f64_to_f16(v: float, lib=None) -> int:
+    """binary16 bits of v, nearest, ties to even."""
+    return int((lib or load_library()).q4o_f64_to_f16(float(v)))
+
+
+QUANT_KINDS = {"f16": 0, "bf16": 1, "f32": 2}
+
+
+def quantize(w, kind: str, lib=None):
+    """Dense weights [N, K] -> (codes uint8 [N, K], scales fp16 bits uint16
+    [N, K/32]) by the block rule stated in q4_oracle.c.  w: uint16 bit
+    patterns for kind "f16" / "bf16", float32 values for "f32"."""
+    k = QUANT_KINDS[kind]
+    w = _c(w, np.float32 if k == 2 else np.uint16)
+    N, K = w.shape
+    if K % 32 or K <= 0:
+        raise ValueError("K must be a positive multiple of 32")
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint16)
+    rc = (lib or load_library()).q4o_quantize(w.ctypes.data_as(ctypes.c_void_p), k, _ptr(codes, ctypes.c_uint8),
+                                              _ptr(scales, ctypes.c_uint16), N, K)
+    if rc != 0:
+        raise RuntimeError("oracle q4o_quantize failed (%d)" % rc)
+    return codes, scales

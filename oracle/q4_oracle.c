@@ -48,7 +48,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#define Q4O_ABI 2
+#define Q4O_ABI 3
 
 int q4o_abi_version(void) { return Q4O_ABI; }
 
@@ -286,4 +286,95 @@ int q4o_linear_sampled(const uint16_t *x, int x_is_bf16, const uint8_t *wq,
         free(xrow);
     }
     return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------- quantizer
+ * The step before pack, which the pages never define: how dense weights
+ * become codes and scales.  The rule (absmax scaling, the plain reading of
+ * a symmetric 4-bit code with offset 8 whose largest magnitude, 7, maps to
+ * the block's largest weight), per block of 32 consecutive weights of a row:
+ *     d = absmax / 7, rounded once to binary16 (nearest, ties to even);
+ *     q = clamp(round_half_even(w / d), -8, 7) + 8, on the exact quotient;
+ *     a block whose d rounds to zero gets d = +0 and every code 8.
+ * Inputs must be finite with absmax / 7 below the binary16 overflow
+ * threshold (65520); other blocks are outside the rule.
+ *
+ * Exactness here: absmax / 7 is rounded to fp64 and then to binary16, which
+ * equals one rounding of the exact quotient (53 >= 2 * 11 + 2 bits); w / d
+ * for w of at most 24 significant bits and d of at most 11 cannot land on a
+ * half-integer by fp64 rounding unless it is one exactly, so nearbyint of
+ * the fp64 quotient is the half-even rounding of the exact quotient.
+ */
+
+/* double -> binary16 bits, nearest, ties to even (overflow -> infinity). */
+uint16_t q4o_f64_to_f16(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (isnan(v))
+        return 0x7E00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);      /* a = m 2^e, m in [0.5, 1) */
+    int E = e - 1;     /* a = (2m) 2^E, 2m in [1, 2) */
+    if (E < -14) {     /* subnormal range: quantum 2^-24 */
+        const double n = nearbyint(ldexp(a, 24));  /* 0 .. 1024 (1024 = smallest normal) */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    double n = nearbyint(ldexp(a, 10 - E));  /* 1024 .. 2048 */
+    if (n == 2048.0) {
+        n = 1024.0;
+        ++E;
+    }
+    if (E > 15)
+        return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)n - 1024));
+}
+
+/* One input element as an exact double: kind 0 binary16 bits, 1 bfloat16
+ * bits (both uint16), 2 IEEE binary32 (float). */
+static double w_value(const void *w, int kind, int64_t i)
+{
+    if (kind == 2)
+        return (double)((const float *)w)[i];
+    const uint16_t b = ((const uint16_t *)w)[i];
+    return kind == 1 ? q4o_bf16_to_f64(b) : q4o_f16_to_f64(b);
+}
+
+/* w [N][K] (kind as above) -> codes uint8 [N][K], scales binary16 bits
+ * [N][K/32].  Returns 0, or -1 for a bad shape or kind. */
+int q4o_quantize(const void *w, int kind, uint8_t *codes, uint16_t *scales, int64_t N, int64_t K)
+{
+    if (N < 0 || K <= 0 || K % 32 != 0 || kind < 0 || kind > 2)
+        return -1;
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t base = n * K + 32 * b;
+            double absmax = 0.0;
+            for (int k = 0; k < 32; ++k) {
+                const double a = fabs(w_value(w, kind, base + k));
+                if (a > absmax)
+                    absmax = a;
+            }
+            const uint16_t dbits = q4o_f64_to_f16(absmax / 7.0);
+            const double d = q4o_f16_to_f64(dbits);
+            scales[n * nb + b] = dbits;
+            for (int k = 0; k < 32; ++k) {
+                int code = 8;
+                if (d != 0.0) {
+                    double q = nearbyint(w_value(w, kind, base + k) / d);
+                    if (q < -8.0)
+                        q = -8.0;
+                    if (q > 7.0)
+                        q = 7.0;
+                    code = (int)q + 8;
+                }
+                codes[base + k] = (uint8_t)code;
+            }
+        }
+    }
+    return 0;
 }

@@ -290,6 +290,120 @@ def pin_special(lib, seed: int = 4) -> None:
         assert np.array_equal(y_all[m], y_one[0]), "row %d depends on the batch" % m
 
 
+# ------------------------------------------------------------ quantizer
+def pin_f16_encoder(lib, seed: int = 8) -> None:
+    """fp64 -> binary16 (nearest, ties to even) against numpy's conversion,
+    on random magnitudes over the whole range, every exact midpoint between
+    neighbouring binary16 values of a random sample, and the edges."""
+    rng = np.random.default_rng(seed)
+    vals = list(rng.uniform(1, 2, 4000) * np.exp2(rng.integers(-30, 17, 4000)) * rng.choice([-1, 1], 4000))
+    b = rng.integers(0, 0x7BFF, 3000)
+    lo, hi = np_f16(b), np_f16(b + 1)
+    vals += list((lo + hi) / 2)                           # exact midpoints: ties
+    vals += list(np.nextafter((lo + hi) / 2, np.inf))     # just above a midpoint
+    vals += [0.0, -0.0, 2.0 ** -25, 2.0 ** -24, 3 * 2.0 ** -26, 65504.0, 65519.99, 65520.0, 1e6, -1e6]
+    for v in vals:
+        got = lib.q4o_f64_to_f16(float(v))
+        with np.errstate(over="ignore"):  # 65520 and above round to infinity
+            ref = int(np.array(v, np.float64).astype(np.float16).view(np.uint16))
+        assert got == ref, "f64 %r -> 0x%04x, numpy 0x%04x" % (v, got, ref)
+
+
+_F16_POS = None
+
+
+def _f16_nearest(v: Fraction) -> int:
+    """Bits of the binary16 value nearest to v >= 0 (ties to the even
+    pattern), by search over every finite positive binary16 value."""
+    global _F16_POS
+    if _F16_POS is None:
+        _F16_POS = [frac_f16(b) for b in range(0x7C00)]
+    import bisect
+    i = bisect.bisect_left(_F16_POS, v)
+    if i == len(_F16_POS):
+        return 0x7C00
+    if _F16_POS[i] == v or i == 0:
+        return i
+    below, above = _F16_POS[i - 1], _F16_POS[i]
+    if v - below < above - v:
+        return i - 1
+    if above - v < v - below:
+        return i
+    return i if i % 2 == 0 else i - 1
+
+
+def exact_quantize(w_vals):
+    """The block rule in exact rational arithmetic: w_vals [N][K] Fractions."""
+    N, K = len(w_vals), len(w_vals[0])
+    codes = np.zeros((N, K), np.uint8)
+    scales = np.zeros((N, K // 32), np.uint16)
+    for n in range(N):
+        for b in range(K // 32):
+            blk = w_vals[n][32 * b:32 * b + 32]
+            dbits = _f16_nearest(max(abs(v) for v in blk) / 7)
+            scales[n, b] = dbits
+            d = frac_f16(dbits)
+            for k, v in enumerate(blk):
+                q = 8 if d == 0 else min(7, max(-8, round(v / d))) + 8  # round(): half to even
+                codes[n, 32 * b + k] = q
+    return codes, scales
+
+
+def pin_quantize(lib, seed: int = 9) -> None:
+    rng = np.random.default_rng(seed)
+    # exact rational brute force, each input kind, with tie-rich blocks
+    for kind in ("f32", "bf16", "f16"):
+        N, K = 3, 96
+        v = rng.normal(0, 0.02, size=(N, K))
+        v[1, :32] = np.round(rng.normal(0, 3, 32)) / 2 * 0.25   # multiples of d/2 when absmax hits 7 d
+        v[1, 0] = 7 * 0.25
+        v[2, 32:64] = 0.0                                       # zero block
+        v[2, 64:96] *= 1e-9                                     # d rounds to zero / subnormal
+        if kind == "f32":
+            w = v.astype(np.float32)
+            fr = [[Fraction(float(t)) for t in row] for row in w]
+        elif kind == "f16":
+            w = v.astype(np.float16).view(np.uint16)
+            fr = [[frac_f16(int(t)) for t in row] for row in w]
+        else:
+            w = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            fr = [[frac_bf16(int(t)) for t in row] for row in w]
+        codes, scales = oracle.quantize(w, kind, lib=lib)
+        ec, es = exact_quantize(fr)
+        assert np.array_equal(scales, es), "quantize scales (%s)" % kind
+        assert np.array_equal(codes, ec), "quantize codes (%s)" % kind
+    # closed form: w = k d0, k in -7..7 with both ends present -> codes k + 8, d = d0
+    k = np.tile(np.arange(-7, 8), 3)[:32].astype(np.float64)
+    k[0], k[1] = 7, -7
+    codes, scales = oracle.quantize((k * 2.0 ** -5)[None, :].astype(np.float32), "f32", lib=lib)
+    assert np.array_equal(codes[0], (k + 8).astype(np.uint8)) and scales[0, 0] == 0x2800, "grid block"
+    # ties go to the even integer: d = 1 (absmax 7), w = +-0.5, +-1.5, 2.5, 3.5
+    w = np.zeros(32, np.float32)
+    w[:8] = [7, 0.5, -0.5, 1.5, -1.5, 2.5, 3.5, -3.5]
+    codes, scales = oracle.quantize(w[None, :], "f32", lib=lib)
+    assert scales[0, 0] == 0x3C00 and list(codes[0, :8]) == [15, 8, 8, 10, 6, 10, 12, 4], "half-even ties"
+    # a scale tie: absmax / 7 exactly midway between two binary16 values
+    mid = (1 + 2.0 ** -10 / 2)  # between 1 and 1 + 2^-10: ties to 1 (even pattern 0x3C00)
+    w = np.zeros(32, np.float32)
+    w[0] = 7 * mid
+    _, scales = oracle.quantize(w[None, :], "f32", lib=lib)
+    assert scales[0, 0] == 0x3C00, "scale tie"
+    w[0] = 7 * (1 + 3 * 2.0 ** -11)  # between 0x3C01 and 0x3C02: ties to 0x3C02
+    _, scales = oracle.quantize(w[None, :], "f32", lib=lib)
+    assert scales[0, 0] == 0x3C02, "scale tie (odd below)"
+    # invariants on random data: codes within 1..15 (the largest magnitude
+    # maps to 7 d), and dequant(quantize(w)) within d/2 of w
+    w = rng.normal(0, 0.02, size=(8, 256)).astype(np.float32)
+    codes, scales = oracle.quantize(w, "f32", lib=lib)
+    d = np.repeat(np_f16(scales), 32, axis=1)
+    assert codes.min() >= 1 and codes.max() <= 15, "code range"
+    assert np.all(np.abs((codes.astype(np.float64) - 8) * d - w) <= d / 2), "round-trip error"
+    # idempotent on its own output: quantizing the dequantized weights gives them back
+    back = ((codes.astype(np.float64) - 8) * d).astype(np.float32)
+    c2, s2 = oracle.quantize(back, "f32", lib=lib)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales), "idempotence"
+
+
 ALL_PINS = {
     "decoders": pin_decoders,
     "hand": pin_hand,
@@ -298,4 +412,6 @@ ALL_PINS = {
     "pack": pin_pack,
     "special": pin_special,
     "tiled": pin_tiled,
+    "f16_encoder": pin_f16_encoder,
+    "quantize": pin_quantize,
 }

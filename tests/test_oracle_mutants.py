@@ -3,7 +3,9 @@
 Each case copies ``oracle/q4_oracle.c``, changes one expression to a
 plausible bug (swapped nibbles, wrong offset, wrong scale index, a dropped
 term, a flipped sign, the wrong input row, a wrong exponent bias, a wrong
-pack shift), compiles the copy on the CPU and checks that at least one pin
+pack shift; in the quantizer a wrong divisor, rounding mode, code offset or
+absmax, and in the binary16 encoder a wrong rounding, bias or subnormal
+quantum), compiles the copy on the CPU and checks that at least one pin
 fails for it.  The real oracle passing every pin is ``test_oracle.py``.
 """
 import os
@@ -39,6 +41,16 @@ MUTANTS = {
                    "wq[n * (K / 2) + j] = (uint8_t)(lo | (hi << 3));"),
     "tiled_pack_shift": ("(uint8_t)(code << (bit % 8));", "(uint8_t)(code << (bit % 4));"),
     "abs_dropped": ("mag += fabs(t);", "mag += t;"),
+    "quant_divisor": ("q4o_f64_to_f16(absmax / 7.0);", "q4o_f64_to_f16(absmax / 8.0);"),
+    "quant_round_away": ("double q = nearbyint(w_value(w, kind, base + k) / d);",
+                         "double q = round(w_value(w, kind, base + k) / d);"),
+    "quant_offset": ("code = (int)q + 8;", "code = (int)q + 7;"),
+    "quant_zero_block": ("int code = 8;", "int code = 0;"),
+    "quant_signed_absmax": ("const double a = fabs(w_value(w, kind, base + k));",
+                            "const double a = w_value(w, kind, base + k);"),
+    "f16_encode_round_away": ("double n = nearbyint(ldexp(a, 10 - E));", "double n = round(ldexp(a, 10 - E));"),
+    "f16_encode_subnormal": ("nearbyint(ldexp(a, 24));", "nearbyint(ldexp(a, 23));"),
+    "f16_encode_bias": ("(uint16_t)((E + 15) << 10)", "(uint16_t)((E + 16) << 10)"),
 }
 
 
