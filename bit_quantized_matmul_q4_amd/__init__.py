@@ -8,7 +8,8 @@ kernels; this module only checks tensors and passes device pointers and the
 current HIP stream.  PyTorch supplies device memory and streams.
 
 Format: blocks of 32 weights along K with one fp16 scale d each, 4-bit codes
-q in 0..15, weight (q - 8) * d.  Canonical inputs: ``codes`` uint8 [N, K]
+q in 0..15, weight (q - 8) * d.  ``quantize`` makes codes and scales from
+dense weights (absmax / 7 scaling, include/q4.h).  Canonical inputs: ``codes`` uint8 [N, K]
 (one code per byte), ``scales`` float16 [N, K/32].  ``pack`` turns them into
 the packed (tiled) form held by a ``Q4Weight``; ``x`` is bfloat16 or float16
 [M, K], ``y`` is float32 [M, N].
@@ -23,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import KERNELS, Q4Error
 
-__all__ = ["Q4Weight", "linear", "pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
+__all__ = ["Q4Weight", "linear", "pack", "quantize", "quantize_pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
            "set_crossover", "segments", "Q4Error", "library_path"]
 
 
@@ -89,6 +90,28 @@ def pack(codes: torch.Tensor, scales: torch.Tensor) -> Q4Weight:
         st = lib.q4_pack(codes.data_ptr(), scales.data_ptr(), wq.data_ptr(), ws.data_ptr(), N, K, _stream(dev))
     _lib.check(st, "q4_pack")
     return Q4Weight(wq, ws, N, K)
+
+
+def quantize(w: torch.Tensor):
+    """Dense weights [N, K] (float32, bfloat16 or float16, on a GPU) ->
+    canonical (codes uint8 [N, K], scales float16 [N, K/32]) for ``pack``.
+    Per block of 32 weights of a row: d = absmax / 7 rounded once to fp16,
+    code = clamp(round_half_even(w / d), -8, 7) + 8 (include/q4.h)."""
+    lib = _lib.load()
+    _need(w, "w", (torch.float32, torch.bfloat16, torch.float16), 2)
+    N, K = w.shape
+    kind = {torch.float32: _lib.Q4_F32, torch.bfloat16: _lib.Q4_BF16, torch.float16: _lib.Q4_F16}[w.dtype]
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, max(K // 32, 0)), dtype=torch.float16, device=w.device)
+    with torch.cuda.device(w.device):
+        st = lib.q4_quantize(w.data_ptr(), kind, codes.data_ptr(), scales.data_ptr(), N, K, _stream(w.device))
+    _lib.check(st, "q4_quantize")
+    return codes, scales
+
+
+def quantize_pack(w: torch.Tensor) -> Q4Weight:
+    """quantize() then pack(): dense weights [N, K] -> Q4Weight."""
+    return pack(*quantize(w))
 
 
 def workspace_bytes(M: int, N: int, K: int, kernel: str = "auto") -> int:

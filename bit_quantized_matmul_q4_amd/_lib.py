@@ -23,6 +23,7 @@ Q4_ERR_WORKSPACE = -6
 
 Q4_F16 = 0
 Q4_BF16 = 1
+Q4_F32 = 2
 
 Q4_AUTO = 0
 Q4_GEMV = 1
@@ -31,13 +32,13 @@ Q4_GEMM = 2
 KERNELS = {"auto": Q4_AUTO, "gemv": Q4_GEMV, "gemm": Q4_GEMM}
 
 EXPORTS = (
-    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_workspace_bytes", "q4_pack",
+    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_workspace_bytes", "q4_pack", "q4_quantize",
     "q4_packed_code_bytes", "q4_packed_scale_bytes",
     "q4_get_crossover", "q4_set_crossover", "q4_segments", "q4_strerror",
     "q4_last_hip_error", "q4_abi_version",
 )
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class Q4Error(RuntimeError):
@@ -66,6 +67,8 @@ def _declare(lib):
     lib.q4_workspace_bytes.restype = sz
     lib.q4_pack.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.q4_pack.restype = i
+    lib.q4_quantize.argtypes = [vp, i, vp, vp, i, i, vp]
+    lib.q4_quantize.restype = i
     lib.q4_packed_code_bytes.argtypes = [i, i]
     lib.q4_packed_code_bytes.restype = sz
     lib.q4_packed_scale_bytes.argtypes = [i, i]

@@ -102,7 +102,7 @@ const char *q4_strerror(int status)
     case Q4_OK: return "ok";
     case Q4_ERR_NULL: return "a required pointer is NULL";
     case Q4_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K >= 32, K % 32 == 0, sizes in range)";
-    case Q4_ERR_ALIGN: return "misaligned pointer (x, Wq: 16 B; packed scales: 8 B; y: 4 B; workspace: 256 B)";
+    case Q4_ERR_ALIGN: return "misaligned pointer (x, Wq, quantizer w and codes: 16 B; packed scales: 8 B; y: 4 B; workspace: 256 B)";
     case Q4_ERR_ENUM: return "unknown dtype or kernel selector";
     case Q4_ERR_HIP: return "HIP launch error (see q4_last_hip_error)";
     case Q4_ERR_WORKSPACE: return "workspace_bytes > 0 with a NULL workspace";
@@ -196,6 +196,21 @@ size_t q4_packed_scale_bytes(int N, int K)
     if (check_shape(1, N, K) != Q4_OK)
         return 0;
     return q4::packed_scale_bytes(N, K);
+}
+
+int q4_quantize(const void *w, int w_dtype, uint8_t *codes, void *scales, int N, int K, void *stream)
+{
+    if (!w || !codes || !scales)
+        return Q4_ERR_NULL;
+    if (w_dtype != Q4_F16 && w_dtype != Q4_BF16 && w_dtype != Q4_F32)
+        return Q4_ERR_ENUM;
+    const int sh = check_shape(1, N, K);
+    if (sh != Q4_OK)
+        return sh;
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+        return Q4_ERR_ALIGN;
+    const int kind = w_dtype == Q4_F32 ? 2 : w_dtype == Q4_BF16 ? 1 : 0;
+    return hip_status(q4::launch_quantize(w, kind, codes, (uint16_t *)scales, N, K, (hipStream_t)stream));
 }
 
 int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,

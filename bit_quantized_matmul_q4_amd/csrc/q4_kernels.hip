@@ -30,6 +30,8 @@
 //    tree order.
 //
 //  * q4_pack_kernel: canonical codes and scales -> the tiled layout.
+//
+//  * q4_quantize_kernel: dense weights -> canonical codes and scales.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -721,6 +723,114 @@ __global__ __launch_bounds__(256) void q4_tree_combine(const float *__restrict__
     y[i] = tree_sum<16>(v, Gk);
 }
 
+// =============================================================== quantize
+// Dense weights -> canonical codes and binary16 scales, one thread per block
+// of 32 weights of a row.  The rule (the pages leave the quantizer open):
+// d = absmax / 7 rounded once to binary16, nearest with ties to even, and
+// q = clamp(round_half_even(w / d), -8, 7) + 8 on the exact quotient; a
+// block whose d rounds to zero gets d = 0 and codes 8.  Both roundings are
+// taken exactly: a float estimate (within one step of the answer whatever
+// the division's accuracy) is corrected by comparisons that are exact in
+// fp32 -- 7 x a binary16 midpoint has at most 15 significant bits, and the
+// residual w - n d is exactly representable, so fma returns it unrounded.
+__device__ __forceinline__ float f16_value(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint32_t f16_bits_rne(float f)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// binary16 bits of absmax / 7, nearest, ties to even (absmax finite, >= 0)
+__device__ __forceinline__ uint32_t q4_scale_bits(float absmax)
+{
+    uint32_t db = f16_bits_rne(absmax / 7.0f);
+    if (db < 0x7BFFu) {  // the midpoint above is finite
+        const float hi = 0.5f * (f16_value(db) + f16_value(db + 1));
+        if (7.0f * hi < absmax || (7.0f * hi == absmax && (db & 1u)))
+            ++db;
+    }
+    if (db > 0u && db < 0x7C00u) {
+        const float lo = 0.5f * (f16_value(db - 1) + f16_value(db));
+        if (7.0f * lo > absmax || (7.0f * lo == absmax && (db & 1u)))
+            --db;
+    }
+    return db;
+}
+
+// code of w for scale d > 0: clamp(round_half_even(w / d), -8, 7) + 8
+__device__ __forceinline__ uint32_t q4_code(float w, float d)
+{
+    float n = __builtin_rintf(w / d);
+    const float r = __builtin_fmaf(-n, d, w);  // w - n d, exact
+    const float h = 0.5f * d;
+    const float ar = __builtin_fabsf(r);
+    if (ar > h || (ar == h && ((int)n & 1)))
+        n += r > 0.0f ? 1.0f : -1.0f;
+    n = __builtin_fminf(__builtin_fmaxf(n, -8.0f), 7.0f);
+    return (uint32_t)(int)(n + 8.0f);
+}
+
+// KIND: 0 binary16, 1 bfloat16, 2 binary32 input.
+template <int KIND>
+__global__ __launch_bounds__(256) void q4_quantize_kernel(const void *__restrict__ w, uint8_t *__restrict__ codes,
+                                                          uint16_t *__restrict__ scales, size_t blocks)
+{
+    const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= blocks)
+        return;
+    float v[32];
+    if constexpr (KIND == 2) {
+        // (float vectors: this compiler miscompiles a bit_cast of an integer
+        // vector's .y/.z/.w component into a read of component 0)
+        const f32x4 *src = (const f32x4 *)((const float *)w + blk * 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const f32x4 t = src[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[4 * j + e] = t[e];
+        }
+    } else {
+        const u32x4 *src = (const u32x4 *)((const uint16_t *)w + blk * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 t = src[j];
+            const uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t b = (wd[h] >> (16 * e)) & 0xFFFFu;
+                    v[8 * j + 2 * h + e] = KIND == 1 ? __builtin_bit_cast(float, b << 16) : f16_value(b);
+                }
+            }
+        }
+    }
+    float absmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+        absmax = __builtin_fmaxf(absmax, __builtin_fabsf(v[k]));
+    const uint32_t db = q4_scale_bits(absmax);
+    const float d = f16_value(db);
+    const bool live = db != 0u && db < 0x7C00u;
+    uint32_t out[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            word |= (live ? q4_code(v[4 * j + e], d) : 8u) << (8 * e);
+        out[j] = word;
+    }
+    u32x4 *dst = (u32x4 *)(codes + blk * 32);
+    dst[0] = (u32x4){out[0], out[1], out[2], out[3]};
+    dst[1] = (u32x4){out[4], out[5], out[6], out[7]};
+    scales[blk] = (uint16_t)db;
+}
+
 // =================================================================== pack
 // One thread per (tile, quad, lane l = 16 g + c): gathers the four words of
 // lane l (codes of k = 32 b + 8 g + r, blocks b = 4q..4q+3 of column
@@ -1119,6 +1229,20 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
     const size_t mn = (size_t)M * N;
     hipLaunchKernelGGL(q4_tree_combine, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
                        (const float *)workspace, y, mn, sh.gk);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void *w, int kind, uint8_t *codes, uint16_t *scales, int N, int K,
+                           hipStream_t stream)
+{
+    const size_t blocks = (size_t)N * (size_t)(K / 32);
+    const dim3 grid((unsigned)((blocks + 255) / 256));
+    if (kind == 2)
+        hipLaunchKernelGGL(q4_quantize_kernel<2>, grid, dim3(256), 0, stream, w, codes, scales, blocks);
+    else if (kind == 1)
+        hipLaunchKernelGGL(q4_quantize_kernel<1>, grid, dim3(256), 0, stream, w, codes, scales, blocks);
+    else
+        hipLaunchKernelGGL(q4_quantize_kernel<0>, grid, dim3(256), 0, stream, w, codes, scales, blocks);
     return hipGetLastError();
 }
 

@@ -25,6 +25,11 @@ size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales_in, uint8_t *wq, uint16_t *scales_out,
                        int N, int K, hipStream_t stream);
 
+// Dense weights [N][K] (kind 0 binary16, 1 bfloat16, 2 binary32) ->
+// canonical codes [N][K] and binary16 scales [N][K/32].
+hipError_t launch_quantize(const void *w, int kind, uint8_t *codes, uint16_t *scales, int N, int K,
+                           hipStream_t stream);
+
 // Sizes of the tiled layout.
 size_t packed_code_bytes(int N, int K);
 size_t packed_scale_bytes(int N, int K);

@@ -58,20 +58,19 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 
 enum q4_status {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,      /* a required pointer is NULL */
     Q4_ERR_SHAPE = -2,     /* M < 1, N < 1, K < 32, K % 32 != 0, K > 2^25, or a size overflows */
-    Q4_ERR_ALIGN = -3,     /* x or Wq not 16-byte aligned, packed scales not 8-byte
-                              aligned, y not 4-byte aligned (see each call) */
+    Q4_ERR_ALIGN = -3,     /* a pointer below the alignment its call states */
     Q4_ERR_ENUM = -4,      /* unknown dtype or kernel selector */
     Q4_ERR_HIP = -5,       /* a HIP call failed (see q4_last_hip_error) */
     Q4_ERR_WORKSPACE = -6  /* workspace_bytes non-zero with a NULL workspace */
 };
 
-enum q4_dtype { Q4_F16 = 0, Q4_BF16 = 1 };
+enum q4_dtype { Q4_F16 = 0, Q4_BF16 = 1, Q4_F32 = 2 /* q4_quantize input only */ };
 
 enum q4_kernel {
     Q4_AUTO = 0, /* matrix-vector kernel if M <= crossover, else matrix-matrix */
@@ -121,6 +120,26 @@ size_t q4_workspace_bytes(int M, int N, int K, int kernel);
  */
 int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
             void *stream);
+
+/*
+ * Quantize dense weights into the canonical form (the input of q4_pack).
+ * The pages only call the weights "4-bit quantized"; the rule used, per
+ * block of 32 consecutive weights of a row (absmax scaling onto the
+ * symmetric codes -7..7 around the offset 8):
+ *     d = absmax / 7, rounded once to binary16 (nearest, ties to even);
+ *     q = clamp(round_half_even(w / d), -8, 7) + 8, on the exact quotient;
+ *     a block whose d rounds to zero gets d = +0 and every code 8.
+ * Both roundings are exact, so the result is bit-reproducible anywhere.
+ *   w        [N][K] row-major, w_dtype Q4_F32, Q4_BF16 or Q4_F16; device,
+ *            16-byte aligned.  Values must be finite with absmax / 7 below
+ *            65520 (the binary16 overflow threshold); a block outside that
+ *            gets unspecified codes and scale (no error is reported).
+ *   codes    uint8 [N][K] (one code 0..15 per byte); device, 16-byte aligned
+ *   scales   binary16 [N][K/32]; device, 2-byte aligned
+ * K must be a positive multiple of 32.  Enqueues on `stream` like the
+ * compute calls; errors as for them (Q4_ERR_ENUM for a bad w_dtype).
+ */
+int q4_quantize(const void *w, int w_dtype, uint8_t *codes, void *scales, int N, int K, void *stream);
 
 /* Bytes of the packed codes and packed scales of an N x K matrix (0 for a
  * bad shape).  Pure host computation. */

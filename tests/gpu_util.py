@@ -132,3 +132,7 @@ class Probe:
         assert rc == 0
         torch.cuda.synchronize()
         return out.cpu().numpy()
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)

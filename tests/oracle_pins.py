@@ -391,8 +391,15 @@ def pin_quantize(lib, seed: int = 9) -> None:
     w[0] = 7 * (1 + 3 * 2.0 ** -11)  # between 0x3C01 and 0x3C02: ties to 0x3C02
     _, scales = oracle.quantize(w[None, :], "f32", lib=lib)
     assert scales[0, 0] == 0x3C02, "scale tie (odd below)"
+    # a subnormal scale rounds coarsely: absmax / 7 = 3.4 x 2^-24 gives
+    # d = 3 x 2^-24, so +-absmax / d = +-7.93 round to +-8 and the clamp
+    # keeps +8 at 7 (code 15) and -8 as it is (code 0)
+    w = np.zeros(32, np.float32)
+    w[0], w[1] = 7 * 3.4 * 2.0 ** -24, -7 * 3.4 * 2.0 ** -24
+    codes, scales = oracle.quantize(w[None, :], "f32", lib=lib)
+    assert scales[0, 0] == 3 and codes[0, 0] == 15 and codes[0, 1] == 0, "clamp with a subnormal scale"
     # invariants on random data: codes within 1..15 (the largest magnitude
-    # maps to 7 d), and dequant(quantize(w)) within d/2 of w
+    # maps to 7 d for normal scales), and dequant(quantize(w)) within d/2 of w
     w = rng.normal(0, 0.02, size=(8, 256)).astype(np.float32)
     codes, scales = oracle.quantize(w, "f32", lib=lib)
     d = np.repeat(np_f16(scales), 32, axis=1)

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_and_strerror(lib):
-    assert lib.q4_abi_version() == 3
+    assert lib.q4_abi_version() == 4
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
     assert lib.q4_strerror(-99) == b"unknown status"
@@ -142,4 +142,14 @@ def test_argument_checks(lib):
     assert lib.q4_pack(FAKE, FAKE, FAKE, FAKE + 4, 4, 64, None) == _lib.Q4_ERR_ALIGN
     assert lib.q4_pack(FAKE, FAKE + 1, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
     assert call(lib, s=FAKE + 4) == _lib.Q4_ERR_ALIGN
+    q = lib.q4_quantize
+    assert q(None, _lib.Q4_F32, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert q(FAKE, _lib.Q4_F32, None, FAKE, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert q(FAKE, _lib.Q4_F32, FAKE, None, 4, 64, None) == _lib.Q4_ERR_NULL
+    assert q(FAKE, 3, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_ENUM
+    assert q(FAKE, _lib.Q4_BF16, FAKE, FAKE, 4, 48, None) == _lib.Q4_ERR_SHAPE
+    assert q(FAKE, _lib.Q4_F16, FAKE, FAKE, 0, 64, None) == _lib.Q4_ERR_SHAPE
+    assert q(FAKE + 8, _lib.Q4_F32, FAKE, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert q(FAKE, _lib.Q4_F32, FAKE + 8, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
+    assert q(FAKE, _lib.Q4_F32, FAKE, FAKE + 1, 4, 64, None) == _lib.Q4_ERR_ALIGN
     assert lib.q4_last_hip_error() == 0

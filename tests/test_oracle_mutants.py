@@ -45,6 +45,7 @@ MUTANTS = {
     "quant_round_away": ("double q = nearbyint(w_value(w, kind, base + k) / d);",
                          "double q = round(w_value(w, kind, base + k) / d);"),
     "quant_offset": ("code = (int)q + 8;", "code = (int)q + 7;"),
+    "quant_upper_clamp": ("if (q > 7.0)\n                        q = 7.0;", "if (q > 8.0)\n                        q = 8.0;"),
     "quant_zero_block": ("int code = 8;", "int code = 0;"),
     "quant_signed_absmax": ("const double a = fabs(w_value(w, kind, base + k));",
                             "const double a = w_value(w, kind, base + k);"),
