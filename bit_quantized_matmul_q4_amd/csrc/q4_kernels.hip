@@ -376,6 +376,19 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // outputs [tpw][MR][16] floats.
 // TC: tiles per combine (2; 1 above 8 rows, where the partials take 4 KB a row)
 static inline int seg_tc(int M) { return M > 8 ? 1 : 2; }
+// Ring depth of the segment form (a multiple of LQ).  Measured on MI355X:
+// 4 stages beat 6, 8 and 10 (a deep per-wave prefetch delays the data each
+// wave needs first and scatters the workgroup's accesses; 2 helps at one row
+// but loses on the widest matrices).
+template <int R, int LQ>
+constexpr int seg_depth()
+{
+#ifdef SEG_DEPTH_FIXED
+    return SEG_DEPTH_FIXED % LQ == 0 ? SEG_DEPTH_FIXED : 6;
+#else
+    return LQ == 3 ? 6 : 4;
+#endif
+}
 
 __device__ __forceinline__ void workgroup_barrier_lds()
 {
@@ -393,7 +406,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
                                                     float *__restrict__ y, int M, int N, int K, Plan plan,
                                                     int tpw)
 {
-    constexpr int D = 6;  // ring depth: a multiple of LQ
+    constexpr int D = seg_depth<R, LQ>();  // ring depth: a multiple of LQ
     static_assert(D % LQ == 0, "ring positions must map to fixed quads");
     extern __shared__ __attribute__((aligned(16))) float seg_lds[];
     const int MR = min(M, 16);
@@ -996,18 +1009,27 @@ static void launch_gemv_v(const GemvArgs &a)
                            a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
 }
 
-// Built variants: x in LDS with an 8-deep ring; x in the ring with a 4-deep
+// Built variants: x in LDS with a 4-deep ring; x in the ring with a 4-deep
 // (split) or 4/8-deep (one stream per wave) ring.
 template <bool BF16, int R>
 static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
 {
     if (sh.xl) {
+#ifdef GEMV_XL_DEPTH
+        constexpr int DX = GEMV_XL_DEPTH;
+#else
+        constexpr int DX = 4;  // measured: 4 beats 6 and 8 (down_proj, M <= 4)
+#endif
         if (sh.split)
-            launch_gemv_v<BF16, R, 8, true, true>(a);
+            launch_gemv_v<BF16, R, DX, true, true>(a);
         else
-            launch_gemv_v<BF16, R, 8, false, true>(a);
+            launch_gemv_v<BF16, R, DX, false, true>(a);
     } else if (sh.split) {
+#ifdef GEMV_SPLIT_DEPTH
+        launch_gemv_v<BF16, R, GEMV_SPLIT_DEPTH, true, false>(a);
+#else
         launch_gemv_v<BF16, R, 4, true, false>(a);
+#endif
     } else if (sh.D == 4) {
         launch_gemv_v<BF16, R, 4, false, false>(a);
     } else {
