@@ -211,7 +211,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     in.x = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
     in.w_lane = 16u * lane;
     in.s_lane = 8u * c;
-    in.x_lane = (uint32_t)min(c, mrows - 1) * (uint32_t)K * 2u + 16u * g;
+    // row slots past the batch read nothing (an offset past the resource's
+    // range returns zeros without a memory access); they only feed output
+    // rows that are never stored
+    in.x_lane = c < mrows ? (uint32_t)c * (uint32_t)K * 2u + 16u * g : x_bytes;
     in.w_off = 0;
     in.s_off = 0;
 
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     // this segment's A operands, once
     const uint32_t x_bytes = (uint32_t)mrows * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
-    const uint32_t x_lane = (uint32_t)min(c, mrows - 1) * (uint32_t)K * 2u + 16u * g;
+    const uint32_t x_lane = c < mrows ? (uint32_t)c * (uint32_t)K * 2u + 16u * g : x_bytes;  // (as in q4_gemv)
     u32x4 xs[LQ][4];
 #pragma unroll
     for (int q = 0; q < LQ; ++q)
@@ -538,7 +541,11 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 // Every wave issues the same number of ring loads per quad (out-of-range
 // ones return zeros without touching memory), so one immediate vmcnt means
 // "this quad has landed" for every wave.
+#ifdef GL_DS_FIXED
+constexpr int GL_DS = GL_DS_FIXED;
+#else
 constexpr int GL_DS = 3;
+#endif
 constexpr int GL_WAVES = 8;
 constexpr int GL_BM = 64, GL_CT = 8;
 
@@ -558,7 +565,7 @@ struct GlGeom {
     static_assert(XCH % GL_WAVES == 0 && GL_CT == GL_WAVES, "even split over the waves");
 };
 
-template <bool BF16>
+template <bool BF16, bool SHORT>
 __global__ __launch_bounds__(512, 2) void q4_gemm_ring(const uint16_t *__restrict__ x,
                                                        const uint8_t *__restrict__ wq,
                                                        const uint16_t *__restrict__ scales,
@@ -646,22 +653,28 @@ __global__ __launch_bounds__(512, 2) void q4_gemm_ring(const uint16_t *__restric
 
         const uint8_t *stg = ring + (qq % GL_DS) * Ge::STAGE;
         const int q = qbeg + qq;
-        const int nq = min(4, plan.nb - 4 * q);
+        // blocks in the quad: 4, except a short last quad (SHORT only, so
+        // the common case has no branch between the block dots)
+        const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
         if (live_tiles) {
-            u32x4 cw[2];
+            u32x4 cw[2], Aq[4][2];
             u32x2 sw[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
                 cw[ct] = *(const u32x4 *)(stg + Ge::XB + (2 * wc + ct) * 1024 + 16 * lane);
                 sw[ct] = *(const u32x2 *)(stg + Ge::XB + Ge::CB + (2 * wc + ct) * 128 + 8 * c);
             }
+            // every A operand of the quad up front: the reads overlap each other
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    Aq[i][rt] = *(const u32x4 *)(stg + ((2 * wr + rt) * 4 + i) * 1024 + 16 * lane);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (i < nq) {
-                    u32x4 A[2], B[2];
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        A[rt] = *(const u32x4 *)(stg + ((2 * wr + rt) * 4 + i) * 1024 + 16 * lane);
+                if (!SHORT || i < nq) {
+                    u32x4 B[2];
+                    const u32x4(&A)[2] = Aq[i];
 #pragma unroll
                     for (int ct = 0; ct < 2; ++ct)
                         B[ct] = dq(i == 0 ? cw[ct].x : i == 1 ? cw[ct].y : i == 2 ? cw[ct].z : cw[ct].w);
@@ -1230,8 +1243,12 @@ static void launch_gemm_ring(const GemmShape &sh, const uint16_t *x, const uint8
                              float *out, int M, int N, int K, const Plan &plan, hipStream_t stream)
 {
     const dim3 grid(sh.nx, sh.ny, sh.gk);
-    hipLaunchKernelGGL((q4_gemm_ring<BF16>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K, plan, sh.gk,
-                       sh.gk > 1 ? 1 : 0);
+    if (plan.nb & 3)
+        hipLaunchKernelGGL((q4_gemm_ring<BF16, true>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K,
+                           plan, sh.gk, sh.gk > 1 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((q4_gemm_ring<BF16, false>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K,
+                           plan, sh.gk, sh.gk > 1 ? 1 : 0);
 }
 
 hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
