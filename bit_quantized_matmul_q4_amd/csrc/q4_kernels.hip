@@ -140,6 +140,14 @@ __device__ __forceinline__ void gemv_x_lds(u32x4 (&xa)[4], const uint8_t *xrow, 
         xa[b] = *(const u32x4 *)(xrow + 256 * q + 64 * b);
 }
 
+// Row slots of a 16-row slice.  Batch row m sits in A-operand row slot
+// 4 (m mod 4) + m / 4, so that element i of a lane group g's accumulator
+// (D row slot 4 g + i) holds batch row 4 i + g: the rows spread over the four
+// lane groups and a lane holds only ceil(rows / 4) of them (R = 1 up to 4
+// rows, 2 up to 8).  A row's block dot does not depend on its slot, so the
+// bits do not change with the placement.
+__device__ __forceinline__ int slot_row(int s) { return 4 * (s & 3) + (s >> 2); }
+
 // Bytes of LDS a row of x takes when staged: padded by 16 so that rows start
 // in different banks.
 __host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t)K * 2u + 16u; }
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     uint8_t *xlds = (uint8_t *)(dyn_lds + (SPLIT ? 0 : 4 * tps * 256));
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = lane >> 4;  // k-slots 8g..8g+7 (A, B); output rows 4g..4g+3 (D)
+    const int g = lane >> 4;  // k-slots 8g..8g+7 (A, B); batch rows g, g+4, .. (D)
     const int c = lane & 15;  // row slot (A); column slot (B, D)
     const int n16 = (N + 15) / 16;
     const int G = plan.G;
@@ -214,7 +222,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     // row slots past the batch read nothing (an offset past the resource's
     // range returns zeros without a memory access); they only feed output
     // rows that are never stored
-    in.x_lane = c < mrows ? (uint32_t)c * (uint32_t)K * 2u + 16u * g : x_bytes;
+    const int xr = slot_row(c);  // the batch row of A row slot c
+    in.x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
     in.w_off = 0;
     in.s_off = 0;
 
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         --left;
         issue_fence();
     }
-    const uint8_t *xrow = xlds + (uint32_t)min(c, mrows - 1) * gemv_xrow_bytes(K) + 16 * g;
+    const uint8_t *xrow = xlds + (uint32_t)min(xr, mrows - 1) * gemv_xrow_bytes(K) + 16 * g;
     if constexpr (XL) {
         // copy the x rows into LDS, 16 bytes per thread and step, in rounds
         // of 8 loads so that each round costs one memory round trip
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     const Dequant<BF16> dq;
-    // accumulators: the R rows a lane can hold (rows 4g .. 4g + R - 1)
+    // accumulators: the R rows a lane can hold (batch rows g + 4 r, r < R)
     float p[R], root[R];
     TreeStack<R, float> stack;
 #pragma unroll
@@ -293,10 +302,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
                             for (int r = 0; r < R; ++r)
                                 root[r] = p[r];
                         } else {  // the tile's root, kept in LDS until the stream ends
-                            float *o = ystage + ((wave * tps + t) * 16 + 4 * g) * 16 + c;
+                            float *o = ystage + ((wave * tps + t) * 16 + g) * 16 + c;
 #pragma unroll
                             for (int r = 0; r < R; ++r)
-                                o[16 * r] = p[r];
+                                o[64 * r] = p[r];
                             ++t;
                         }
                         li = 0;
@@ -329,12 +338,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             const int n = 16 * (t0 + k) + c;
             if (n >= N)
                 break;
-            const float *o = ystage + ((wave * tps + k) * 16 + 4 * g) * 16 + c;
-            float *yo = y + (size_t)(m0 + 4 * g) * N + n;
+            const float *o = ystage + ((wave * tps + k) * 16 + g) * 16 + c;
+            float *yo = y + (size_t)(m0 + g) * N + n;
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                if (4 * g + r < mrows)
-                    yo[r * (size_t)N] = o[16 * r];
+                if (4 * r + g < mrows)
+                    yo[4 * r * (size_t)N] = o[64 * r];
         }
     }
     if constexpr (SPLIT) {
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         float *rw = red + wave * 16 * 17;
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            rw[(4 * g + r) * 17 + c] = root[r];
+            rw[(4 * r + g) * 17 + c] = root[r];
         __syncthreads();
         for (int o = threadIdx.x; o < TW * 256; o += blockDim.x) {
             const int slot = o >> 8, row = (o >> 4) & 15, col = o & 15;
@@ -431,7 +440,8 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     // this segment's A operands, once
     const uint32_t x_bytes = (uint32_t)mrows * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
-    const uint32_t x_lane = c < mrows ? (uint32_t)c * (uint32_t)K * 2u + 16u * g : x_bytes;  // (as in q4_gemv)
+    const int xr = slot_row(c);  // (as in q4_gemv)
+    const uint32_t x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
     u32x4 xs[LQ][4];
 #pragma unroll
     for (int q = 0; q < LQ; ++q)
@@ -486,8 +496,8 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
                     float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        if (4 * g + r < mrows)
-                            rt[(4 * g + r) * 16 + c] = p[r];
+                        if (4 * r + g < mrows)
+                            rt[(4 * r + g) * 16 + c] = p[r];
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         p[r] = 0.f;
@@ -1129,7 +1139,7 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
     if (!e_seg || plan.S != 16)
         return false;
     LQ = (plan.G + 15) / 16;
-    if (LQ > 3 || (LQ == 3 && M >= 3))  // 3-quad segments at 4 rows: 128 registers do not hold them
+    if (LQ > 3 || (LQ == 3 && M > 8))  // 3-quad segments at R = 4: 128 registers do not hold them
         return false;
     const int tiles = (N + 15) / 16;
     // measured on MI355X: with one tile per workgroup or fewer (N <= 4096)
@@ -1146,7 +1156,9 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
                        float *y, int M, int N, int K, hipStream_t stream)
 {
     const Plan plan = make_plan(K);
-    const int R = M >= 3 ? 4 : M;
+    // accumulator rows per lane: ceil(rows / 4), with 3 rounded up to 4
+    const int rows = M < 16 ? M : 16;
+    const int R = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;
     {
         int LQ, tpw;
         size_t lds;
@@ -1198,7 +1210,7 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     a.L = sh.L;
     a.tps = sh.tps;
     a.plan = plan;
-    // every 16-row slice but a last short one has 16 rows; 3 rows use R = 4
+    // every 16-row slice but a last short one has 16 rows
     if (bf16)
         launch_gemv_b<true>(R, sh, a);
     else
