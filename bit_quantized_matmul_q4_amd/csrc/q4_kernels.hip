@@ -227,6 +227,37 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     in.w_off = 0;
     in.s_off = 0;
 
+    // XL: x is copied into LDS, 16 bytes per thread and step, in rounds of 8
+    // loads so that each round costs one memory round trip.  The first
+    // round's loads go out ahead of the ring's prefill: x is what every wave
+    // needs first, and behind the prefill they would wait for the first
+    // stages of the whole grid.  Chunks past the rows fall outside x's range
+    // (zero, no memory access) and land in the slack past the rows: with a
+    // conditional store the compiler sinks the load into it, behind a wait
+    // for the whole prefill.
+    const int cpr = K / 8;  // 16-byte chunks per row
+    const int nch = mrows * cpr;
+    u32x4 xv[8];
+    auto x_round_load = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t i = (uint32_t)(i0 + u * (int)blockDim.x + (int)threadIdx.x);
+            xv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, i * 16u, 0, 0));
+        }
+    };
+    auto x_round_store = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = min(i0 + u * (int)blockDim.x + (int)threadIdx.x, nch);
+            const int r = i / cpr;  // mrows for the slack
+            *(u32x4 *)(xlds + (uint32_t)r * gemv_xrow_bytes(K) + (uint32_t)(i - r * cpr) * 16u) = xv[u];
+        }
+    };
+    if constexpr (XL) {
+        x_round_load(0);
+        issue_fence();
+    }
+
     GemvStage ring[D];
     int ql = q0;     // quad of the next stage to load
     int left = total;  // loads left that the stream uses
@@ -239,28 +270,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     }
     const uint8_t *xrow = xlds + (uint32_t)min(xr, mrows - 1) * gemv_xrow_bytes(K) + 16 * g;
     if constexpr (XL) {
-        // copy the x rows into LDS, 16 bytes per thread and step, in rounds
-        // of 8 loads so that each round costs one memory round trip
-        const int cpr = K / 8;  // 16-byte chunks per row
-        const int nch = mrows * cpr;
-        for (int i0 = 0; i0 < nch; i0 += 8 * (int)blockDim.x) {
-            u32x4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = min(i0 + u * (int)blockDim.x + (int)threadIdx.x, nch - 1);
-                const int r = i / cpr;
-                v[u] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, (uint32_t)i * 16u, 0, 0));
-                (void)r;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
-                if (i < nch) {
-                    const int r = i / cpr;
-                    *(u32x4 *)(xlds + (uint32_t)r * gemv_xrow_bytes(K) + (uint32_t)(i - r * cpr) * 16u) = v[u];
-                }
-            }
+        x_round_store(0);
+        for (int i0 = 8 * (int)blockDim.x; i0 < nch; i0 += 8 * (int)blockDim.x) {
+            x_round_load(i0);
+            x_round_store(i0);
         }
         __syncthreads();
     }
