@@ -23,11 +23,15 @@ ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 # No fast-math, no FMA contraction (the reduction order uses explicit fmaf),
 # and no packed fp32 instructions.  Matrix-core results go to ordinary vector
 # registers (the accumulator-register form costs a read-back per element).
+# No sinking of common code out of branches: it merges the tree stack's
+# per-level writes into one store with a computed address, which moves the
+# whole stack to scratch memory.
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-mllvm", "-simplifycfg-sink-common=false",
     "-I", os.path.join(ROOT, "include"),
 ]
 

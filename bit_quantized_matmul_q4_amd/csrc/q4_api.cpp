@@ -23,9 +23,10 @@ namespace {
 
 // Measured GEMV -> GEMM crossover on MI355X (rows); M <= T runs the GEMV.
 // On the Qwen2.5-7B-shaped layer set (the sum of the six projections' times)
-// the matrix-matrix kernel first wins at M = 33, where the matrix-vector
-// kernel needs a third 16-row slice; at 32 it is still 3% slower.  T = 32.
-constexpr int kDefaultCrossover = 32;
+// the matrix-matrix kernel first wins at M = 17, where the matrix-vector
+// kernel needs a second 16-row slice (102 vs 106 us); at 16 the matrix-vector
+// kernel is 10% faster (73 vs 81 us).  T = 16.
+constexpr int kDefaultCrossover = 16;
 
 thread_local int g_last_hip = 0;
 

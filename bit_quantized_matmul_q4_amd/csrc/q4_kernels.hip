@@ -20,14 +20,13 @@
 //    owns segment j of all of them and holds that segment of x in
 //    registers, so the workgroup reads x once.
 //
-//  * q4_gemm_ring: the LDS-staged tile kernel for larger M.  A workgroup of
-//    eight waves owns a 64 x 128 output unit; per quad, the activation
-//    chunk, code tiles and scales stream into a ring in LDS by direct
-//    global-to-LDS loads, each wave dequantizes the code words of its two
-//    column tiles in registers and runs 2 x 2 MFMA tiles from LDS.  K may be
-//    split across workgroups (one subtree of segments each) when a
-//    workspace is given; q4_tree_combine then joins the subtree roots in
-//    tree order.
+//  * q4_gemm_ws: the matrix-matrix kernel for larger M.  A workgroup of
+//    4..8 waves owns an output unit of 16 or 32 rows by one column tile per
+//    wave; each wave streams its tile's codes and scales through a register
+//    ring and reads the unit's activations from an LDS ring filled by direct
+//    global-to-LDS loads.  K may be split across workgroups (one subtree of
+//    segments each) when a workspace is given; q4_tree_combine then joins
+//    the subtree roots in tree order.
 //
 //  * q4_pack_kernel: canonical codes and scales -> the tiled layout.
 //
@@ -546,216 +545,232 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 }
 
 // =================================================================== GEMM
-// The streaming matrix-matrix kernel.  A workgroup of eight waves owns one
-// output unit of 64 rows by 128 columns (4 x 8 tiles of 16 x 16) and one
-// K-group; wave w computes the 2 x 2 tile block at row tiles 2 (w / 4), +1
-// and column tiles 2 (w % 4), +1.
-//
-// Per quad, the inputs arrive in a GL_DS-deep LDS ring by direct
-// global-to-LDS loads (no registers held in flight): the 64 x 128
-// activation chunk in A-operand order (lane l's 16 bytes at 16 l), the
-// unit's 8 code tiles and their scales.  Each wave reads its two column
-// tiles' code words and dequantizes them in registers (a column tile is
-// dequantized by the two waves that use it, which costs less than a round
-// trip of the operands through LDS); the correction dot E of a row tile
-// serves both column tiles.  One barrier per quad; segment partials fold
-// into the streaming pairwise tree in registers.
-//
-// Every wave issues the same number of ring loads per quad (out-of-range
-// ones return zeros without touching memory), so one immediate vmcnt means
-// "this quad has landed" for every wave.
-#ifdef GL_DS_FIXED
-constexpr int GL_DS = GL_DS_FIXED;
-#else
-constexpr int GL_DS = 3;
-#endif
-constexpr int GL_WAVES = 8;
-constexpr int GL_BM = 64, GL_CT = 8;
-
 // s_waitcnt immediate: vmcnt <= n (n < 64), expcnt and lgkmcnt not waited.
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-struct GlGeom {
-    static constexpr int RT = GL_BM / 16;               // row tiles per unit
-    static constexpr int XCH = RT * 4;                  // activation chunks (row tile, block)
-    static constexpr int XPW = XCH / GL_WAVES;          // ... per wave
-    static constexpr int XB = XCH * 1024;
-    static constexpr int CB = GL_CT * 1024;             // code tiles, one per wave
-    static constexpr int SB = 2 * GL_WAVES * 128;       // scales, two tile slots per wave
-    static constexpr int STAGE = XB + CB + SB;
-    static constexpr int LOADS = XPW + 2;               // ring loads per wave per quad
-    static constexpr int BYTES = GL_DS * STAGE;
-    static_assert(XCH % GL_WAVES == 0 && GL_CT == GL_WAVES, "even split over the waves");
-};
+// The weight-streaming matrix-matrix kernel.  A workgroup of CT waves
+// (CT = blockDim / 64, 4..8) owns an output unit of 16 RT rows (RT = 1, 2) by
+// CT column tiles and one K-group; wave w computes column tile w of the unit
+// for all RT row tiles.  The wave streams its tile's codes and scales
+// through a GW_DW-deep register ring (the matrix-vector kernel's loads;
+// refills past the K-group's end fall outside the resources' exact ranges
+// and read nothing), so every weight byte a workgroup needs is loaded once,
+// by the wave that uses it, with many bytes in flight.  The unit's
+// activations, 16 RT rows by 128 k per quad in A-operand lane order (chunk
+// (row tile, block): lane l's 16 bytes at 16 l), arrive in a GW_XS-deep LDS
+// ring by direct global-to-LDS loads spread over the waves; every wave
+// issues RT of them per quad (chunks past the stage go to a 1 KB placeholder
+// target and read nothing), so one immediate vmcnt and one barrier per quad
+// order the ring.  Per block a wave dequantizes its B operand once for its
+// RT row tiles and runs 2 RT block dots (D and the correction E of each row
+// tile).
+//
+// The grid is one-dimensional over (column unit, row unit) and K-groups in y:
+// workgroup id -> column unit 8 (id / 8 nru) + id % 8, row unit (id / 8) %
+// nru, so the row units of one column unit (which read the same weights) are
+// eight ids apart: dispatched together, on the same XCD and its L2.
+#ifdef GW_XS_FIXED
+constexpr int GW_XS = GW_XS_FIXED;
+#else
+constexpr int GW_XS = 3;  // x ring stages (LDS)
+#endif
+#ifdef GW_DW_FIXED
+constexpr int GW_DW = GW_DW_FIXED;
+#else
+constexpr int GW_DW = 4;  // weight ring stages (registers)
+#endif
 
-template <bool BF16, bool SHORT>
-__global__ __launch_bounds__(512, 2) void q4_gemm_ring(const uint16_t *__restrict__ x,
-                                                       const uint8_t *__restrict__ wq,
-                                                       const uint16_t *__restrict__ scales,
-                                                       float *__restrict__ out, int M, int N, int K, Plan plan,
-                                                       int Gk, int write_partial)
+// One quad of a wave's column tile for its RT row tiles: codes w and
+// scales s from the register ring, the A operands from the LDS stage stg.
+// (Software-pipelining the blocks, block dots of block i before the
+// scale-accumulate of block i - 1, measured faster only at three and four
+// row tiles, whose units lose to smaller ones; at one or two row tiles its
+// registers cost occupancy.)
+template <bool BF16, int RT, bool SHORT>
+__device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *stg, int lane, int nq,
+                                             const Dequant<BF16> &dq, f32x4 (&p)[RT])
 {
-    typedef GlGeom Ge;
-    typedef __attribute__((address_space(3))) void lds_t;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[Ge::BYTES];
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!SHORT || i < nq) {
+            const u32x4 B = dq(wd[i]);
+            u32x4 A[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                A[rt] = *(const u32x4 *)(stg + (rt * 4 + i) * 1024 + 16 * lane);
+            // the block dots first, so they overlap in the matrix pipe
+            f32x4 E[RT], Dm[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                E[rt] = blockdot<BF16>(A[rt], dq.offset);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                Dm[rt] = blockdot<BF16>(A[rt], B);
+            const uint32_t sd = i < 2 ? s.x : s.y;
+            const float dsc = half_bits_to_float((i & 1) ? sd >> 16 : sd & 0xFFFFu);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                scale_accumulate(p[rt], dsc, Dm[rt], E[rt]);
+        }
+    }
+}
 
+template <bool BF16, int RT, bool SHORT>
+__global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x, const uint8_t *__restrict__ wq,
+                                                  const uint16_t *__restrict__ scales, float *__restrict__ out,
+                                                  int M, int N, int K, Plan plan, int Gk, int ncu, int nru,
+                                                  int write_partial)
+{
+    typedef __attribute__((address_space(3))) void lds_t;
+    constexpr int NCH = 4 * RT;  // x chunks per stage
+    constexpr int XSTAGE = NCH * 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[GW_XS * XSTAGE + 1024];
+    uint8_t *const xdummy = xring + GW_XS * XSTAGE;  // the placeholders' target, never read
+
+    const int CT = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wr = w >> 2, wc = w & 3;
     const int g = lane >> 4, c = lane & 15;
-    const int m0 = blockIdx.y * GL_BM;
-    const int mrows = __builtin_amdgcn_readfirstlane(min(GL_BM, M - m0));
+    const int id = blockIdx.x;
+    const int cu = 8 * (id / (8 * nru)) + id % 8;
+    const int ru = (id / 8) % nru;
+    if (cu >= ncu)
+        return;  // the whole workgroup, before any barrier
+    const int m0 = ru * 16 * RT;
+    const int mrows = __builtin_amdgcn_readfirstlane(min(16 * RT, M - m0));
     const int G = plan.G;
     const int n16 = (N + 15) / 16;
-    const int tb = blockIdx.x * GL_CT;  // first column tile of the unit
-    const int nct = __builtin_amdgcn_readfirstlane(min(GL_CT, n16 - tb));
+    const int ct = cu * CT + w;  // the wave's column tile
+    const bool live_ct = ct < n16;
     // K-group: segments [j0, j0 + L), quads [qbeg, qend)
     const int L = plan.S / Gk;
-    const int j0 = blockIdx.z * L;
+    const int j0 = blockIdx.y * L;
     const int qbeg = (j0 * G) >> plan.log2S;
     const int qend = ((j0 + L) * G) >> plan.log2S;
     const int nquads = qend - qbeg;
 
-    // ring load sources (resources in scalar registers: ranges via readfirstlane)
+    // x rows m0 .. m0 + mrows - 1 (rows past them: offsets past the range)
     const uint32_t xrow = 2u * (uint32_t)K;
     const uint32_t x_range = __builtin_amdgcn_readfirstlane(mrows * (int)xrow);
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_range);
-    const uint32_t tile_b = (uint32_t)G * 1024u, tile_s = (uint32_t)G * 128u;
-    const uint32_t w_range = __builtin_amdgcn_readfirstlane(nct * (int)tile_b);
-    const uint32_t s_range = __builtin_amdgcn_readfirstlane(nct * (int)tile_s);
-    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + (size_t)tb * G * 1024, w_range);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + (size_t)tb * G * 64, s_range);
+    // the wave's tile, quads qbeg .. qend - 1 (a spare wave: empty ranges)
+    const size_t tq = (size_t)min(ct, n16 - 1) * G + qbeg;
+    const uint32_t w_range = __builtin_amdgcn_readfirstlane(live_ct ? nquads * 1024 : 0);
+    const uint32_t s_range = __builtin_amdgcn_readfirstlane(live_ct ? nquads * 128 : 0);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + tq * 1024, w_range);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + tq * 64, s_range);
 
-    // quad qq of the run into its ring stage (qq >= nquads: placeholders)
-    auto issue = [&](int qq) {
-        uint8_t *stg = ring + (qq % GL_DS) * Ge::STAGE;
+    auto issue_x = [&](int qq) {  // quad qq of the K-group into its stage
+        uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
         const bool live = qq < nquads;
         const int q = qbeg + qq;
 #pragma unroll
-        for (int h = 0; h < Ge::XPW; ++h) {
-            const int ch = w + GL_WAVES * h;  // chunk = rt * 4 + i
+        for (int h = 0; h < RT; ++h) {
+            const int ch = w + CT * h;  // chunk = row tile * 4 + block
+            const bool real = ch < NCH;
             const int rt = ch >> 2, i = ch & 3;
-            const uint32_t off = live ? (uint32_t)(16 * rt + c) * xrow + 256u * q + 64u * i + 16u * g : x_range;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(stg + ch * 1024), 16, off, 0, 0, 0);
-        }
-        {
-            const int ct = w;
-            const uint32_t off = live && ct < nct ? (uint32_t)ct * tile_b + 1024u * q + 16u * lane : w_range;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_t *)(stg + Ge::XB + ct * 1024), 16, off, 0, 0, 0);
-        }
-        {
-            const int ct = 2 * w + (lane >> 5);
-            const uint32_t off = live && ct < nct ? (uint32_t)ct * tile_s + 128u * q + 4u * (lane & 31) : s_range;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)(stg + Ge::XB + Ge::CB + w * 256), 4, off, 0, 0,
-                                                     0);
+            const uint32_t off =
+                live && real ? (uint32_t)(16 * rt + c) * xrow + 256u * q + 64u * i + 16u * g : x_range;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(real ? stg + ch * 1024 : xdummy), 16, off, 0,
+                                                     0, 0);
         }
     };
+    struct WStage {
+        u32x4 w;
+        u32x2 s;
+    };
+    WStage ring[GW_DW];
+    uint32_t w_off = 0, s_off = 0;
+    auto issue_w = [&](WStage &st) {
+        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane, w_off, 0));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 8u * c, s_off, 0));
+        w_off += 1024u;
+        s_off += 128u;
+    };
+
+    // Issue order: x stages 0 .. GW_XS - 2, weight stages 0 .. GW_DW - 1;
+    // then per quad t: [wait, barrier] x stage t + GW_XS - 1, compute t,
+    // weight refill t + GW_DW.  Loads issued after x stage t by the top of
+    // quad t: at least the refill of its own quad and GW_XS - 2 quads of both
+    // kinds (more in the prologue), so waiting for that many to remain
+    // outstanding lands x stage t; weight stage t (issued earlier, as
+    // GW_DW > GW_XS - 1) with it.
+    constexpr int XWAIT = 2 + (GW_XS - 2) * (RT + 2);
+    static_assert(GW_DW > GW_XS - 1, "the weight stage must precede its x stage");
+#pragma unroll
+    for (int s2 = 0; s2 < GW_XS - 1; ++s2) {
+        issue_x(s2);
+        issue_fence();
+    }
+#pragma unroll
+    for (int d = 0; d < GW_DW; ++d) {
+        issue_w(ring[d]);
+        issue_fence();
+    }
 
     const Dequant<BF16> dq;
-    f32x4 p[4];  // [rt][ct] of the wave's 2 x 2 tiles
-    TreeStack<4, f32x4> stack;
+    f32x4 p[RT];
+    TreeStack<RT, f32x4> stack;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < RT; ++a)
         p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
     int li = 0;
     int seg_end = ((j0 + 1) * G) >> plan.log2S;
-    const bool live_tiles = 32 * wr < mrows && 2 * wc < nct;  // wave-uniform
 
+    for (int base = 0; base < nquads; base += GW_DW) {
 #pragma unroll
-    for (int s = 0; s < GL_DS - 1; ++s)
-        issue(s);
+        for (int d = 0; d < GW_DW; ++d) {
+            const int qq = base + d;
+            if (qq < nquads) {
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(XWAIT));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                issue_x(qq + GW_XS - 1);
+                issue_fence();
 
-    for (int qq = 0; qq < nquads; ++qq) {
-        // quad qq landed (this wave's loads, in order; then everyone's), and
-        // every wave is done with quad qq - 1, whose stage the next loads take
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((GL_DS - 2) * Ge::LOADS));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue(qq + GL_DS - 1);
-
-        const uint8_t *stg = ring + (qq % GL_DS) * Ge::STAGE;
-        const int q = qbeg + qq;
-        // blocks in the quad: 4, except a short last quad (SHORT only, so
-        // the common case has no branch between the block dots)
-        const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
-        if (live_tiles) {
-            u32x4 cw[2], Aq[4][2];
-            u32x2 sw[2];
+                const uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
+                const int q = qbeg + qq;
+                // blocks in the quad: 4, except a short last quad (SHORT only)
+                const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
+                if (live_ct)
+                    gemm_ws_quad<BF16, RT, SHORT>(ring[d].w, ring[d].s, stg, lane, nq, dq, p);
+                if (q + 1 == seg_end) {  // segment j0 + li done
+                    if (!stack.push_branch(p, li, L)) {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                cw[ct] = *(const u32x4 *)(stg + Ge::XB + (2 * wc + ct) * 1024 + 16 * lane);
-                sw[ct] = *(const u32x2 *)(stg + Ge::XB + Ge::CB + (2 * wc + ct) * 128 + 8 * c);
-            }
-            // every A operand of the quad up front: the reads overlap each other
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    Aq[i][rt] = *(const u32x4 *)(stg + ((2 * wr + rt) * 4 + i) * 1024 + 16 * lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (!SHORT || i < nq) {
-                    u32x4 B[2];
-                    const u32x4(&A)[2] = Aq[i];
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
-                        B[ct] = dq(i == 0 ? cw[ct].x : i == 1 ? cw[ct].y : i == 2 ? cw[ct].z : cw[ct].w);
-                    // the six block dots first, so they overlap in the matrix pipe
-                    f32x4 E[2], Dm[4];
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        E[rt] = blockdot<BF16>(A[rt], dq.offset);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int ct = 0; ct < 2; ++ct)
-                            Dm[2 * rt + ct] = blockdot<BF16>(A[rt], B[ct]);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) {
-                            const uint32_t sd = i < 2 ? sw[ct].x : sw[ct].y;
-                            const float d = half_bits_to_float((i & 1) ? sd >> 16 : sd & 0xFFFFu);
-                            scale_accumulate(p[2 * rt + ct], d, Dm[2 * rt + ct], E[rt]);
-                        }
+                        for (int a = 0; a < RT; ++a)
+                            p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    }
+                    ++li;
+                    seg_end = ((j0 + li + 1) * G) >> plan.log2S;
                 }
+                issue_fence();
+                issue_w(ring[d]);  // quad qq + GW_DW (past the end: reads nothing)
+                issue_fence();
             }
-        }
-        if (q + 1 == seg_end) {  // segment j0 + li done
-            if (!stack.push_branch(p, li, L)) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-            ++li;
-            seg_end = ((j0 + li + 1) * G) >> plan.log2S;
         }
     }
     // the placeholder loads land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // p holds the K-group's subtree roots
+    const int n = 16 * ct + c;
+    if (live_ct && n < N) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int n = 16 * (tb + 2 * wc + ct) + c;
-            if (n >= N)
-                continue;
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int m = m0 + 32 * wr + 16 * rt + 4 * g + e;
-                if (m >= M)
-                    continue;
-                const f32x4 v4 = p[2 * rt + ct];
-                const float v = e == 0 ? v4.x : e == 1 ? v4.y : e == 2 ? v4.z : v4.w;
-                if (write_partial)
-                    out[((size_t)blockIdx.z * M + m) * N + n] = v;
-                else
-                    out[(size_t)m * N + n] = v;
+                const int m = m0 + 16 * rt + 4 * g + e;
+                if (m < M) {
+                    const float v = e == 0 ? p[rt].x : e == 1 ? p[rt].y : e == 2 ? p[rt].z : p[rt].w;
+                    if (write_partial)
+                        out[((size_t)blockIdx.y * M + m) * N + n] = v;
+                    else
+                        out[(size_t)m * N + n] = v;
+                }
             }
-        }
+    }
 }
 
 // Joins Gk subtree roots (workspace [Gk][M][N]) in pairwise-tree order.
@@ -1231,23 +1246,39 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     return hipGetLastError();
 }
 
-// Streaming matrix-matrix kernel shape: 64 x 128 units, K split over Gk
-// groups when a workspace allows and the grid would otherwise hold fewer
-// than about two units per compute unit.
-struct GemmShape {
-    int nx, ny, gk;
-};
-
 static constexpr int kComputeUnits = 256;
 
-static GemmShape gemm_shape(int M, int N, int K, size_t workspace_bytes)
+// Matrix-matrix shape: row units of 16 RT rows (the rows spread evenly over
+// the units), column units of CT tiles (one wave each), K split over Gk
+// groups when a workspace allows and the grid would otherwise leave compute
+// units idle.  Measured on MI355X (7B shapes, M = 17..124): 16-row units
+// beat 32-, 48- and 64-row ones for K <= 8192 and 32-row units win for
+// K = 18944 (the row units of a column unit read its weights from one L2,
+// and small units keep occupancy up and LDS traffic down).
+struct GemmWsShape {
+    int RT, nru, CT, ncu, gk;
+};
+
+static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
 {
     const Plan plan = make_plan(K);
-    GemmShape sh;
-    sh.ny = (M + GL_BM - 1) / GL_BM;
-    sh.nx = ((N + 15) / 16 + GL_CT - 1) / GL_CT;
+    GemmWsShape sh;
+    static const int e_rt = env_knob("Q4_GEMM_RT", 0);  // for measurement
+    int rt = K > 8192 ? 2 : 1;
+    if (e_rt == 1 || e_rt == 2)
+        rt = e_rt;
+    // 16 RT rows of x stay below 2^31 bytes (32-bit offsets)
+    if ((long long)32 * rt * K >= (1LL << 31))
+        rt = 1;  // (K <= 2^25 keeps 16 rows below 2^31 bytes)
+    sh.nru = (M + 16 * rt - 1) / (16 * rt);
+    const int rows = (M + sh.nru - 1) / sh.nru;
+    sh.RT = (rows + 15) / 16;
+    const int tiles = (N + 15) / 16;
+    static const int e_ct = env_knob("Q4_GEMM_CT", 0);
+    sh.CT = e_ct >= 4 && e_ct <= 8 ? e_ct : 8;
+    sh.ncu = (tiles + sh.CT - 1) / sh.CT;
     sh.gk = 1;
-    while (sh.gk < plan.S && (long long)sh.nx * sh.ny * sh.gk < 2 * kComputeUnits &&
+    while (sh.gk < plan.S && (long long)sh.ncu * sh.nru * sh.gk < kComputeUnits &&
            (size_t)(2 * sh.gk) * M * N * sizeof(float) <= workspace_bytes)
         sh.gk *= 2;
     static const int e_gk = env_knob("Q4_GEMM_GK", 0);  // for measurement: forced split (power of two)
@@ -1259,21 +1290,33 @@ static GemmShape gemm_shape(int M, int N, int K, size_t workspace_bytes)
 
 size_t gemm_workspace_bytes(int M, int N, int K)
 {
-    const GemmShape sh = gemm_shape(M, N, K, (size_t)-1);
-    return sh.gk > 1 ? (size_t)sh.gk * M * N * sizeof(float) : 0;
+    const int gk = gemm_ws_shape(M, N, K, (size_t)-1).gk;
+    return gk > 1 ? (size_t)gk * M * N * sizeof(float) : 0;
+}
+
+template <bool BF16, int RT>
+static void launch_gemm_ws_r(const GemmWsShape &sh, const uint16_t *x, const uint8_t *wq, const uint16_t *scales,
+                             float *out, int M, int N, int K, const Plan &plan, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((sh.ncu + 7) / 8 * 8 * sh.nru), (unsigned)sh.gk);
+    const dim3 block((unsigned)(64 * sh.CT));
+    const int wp = sh.gk > 1 ? 1 : 0;
+    if (plan.nb & 3)
+        hipLaunchKernelGGL((q4_gemm_ws<BF16, RT, true>), grid, block, 0, stream, x, wq, scales, out, M, N, K, plan,
+                           sh.gk, sh.ncu, sh.nru, wp);
+    else
+        hipLaunchKernelGGL((q4_gemm_ws<BF16, RT, false>), grid, block, 0, stream, x, wq, scales, out, M, N, K, plan,
+                           sh.gk, sh.ncu, sh.nru, wp);
 }
 
 template <bool BF16>
-static void launch_gemm_ring(const GemmShape &sh, const uint16_t *x, const uint8_t *wq, const uint16_t *scales,
-                             float *out, int M, int N, int K, const Plan &plan, hipStream_t stream)
+static void launch_gemm_ws(const GemmWsShape &sh, const uint16_t *x, const uint8_t *wq, const uint16_t *scales,
+                           float *out, int M, int N, int K, const Plan &plan, hipStream_t stream)
 {
-    const dim3 grid(sh.nx, sh.ny, sh.gk);
-    if (plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemm_ring<BF16, true>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K,
-                           plan, sh.gk, sh.gk > 1 ? 1 : 0);
+    if (sh.RT == 1)
+        launch_gemm_ws_r<BF16, 1>(sh, x, wq, scales, out, M, N, K, plan, stream);
     else
-        hipLaunchKernelGGL((q4_gemm_ring<BF16, false>), grid, dim3(512), 0, stream, x, wq, scales, out, M, N, K,
-                           plan, sh.gk, sh.gk > 1 ? 1 : 0);
+        launch_gemm_ws_r<BF16, 2>(sh, x, wq, scales, out, M, N, K, plan, stream);
 }
 
 hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
@@ -1281,18 +1324,20 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
                        hipStream_t stream)
 {
     const Plan plan = make_plan(K);
-    const GemmShape sh = gemm_shape(M, N, K, workspace ? workspace_bytes : 0);
-    float *out = sh.gk > 1 ? (float *)workspace : y;
+    const size_t ws = workspace ? workspace_bytes : 0;
+    const GemmWsShape sh = gemm_ws_shape(M, N, K, ws);
+    const int gk = sh.gk;
+    float *out = gk > 1 ? (float *)workspace : y;
     if (bf16)
-        launch_gemm_ring<true>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
+        launch_gemm_ws<true>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
     else
-        launch_gemm_ring<false>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
+        launch_gemm_ws<false>(sh, (const uint16_t *)x, wq, scales, out, M, N, K, plan, stream);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || sh.gk == 1)
+    if (e != hipSuccess || gk == 1)
         return e;
     const size_t mn = (size_t)M * N;
     hipLaunchKernelGGL(q4_tree_combine, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
-                       (const float *)workspace, y, mn, sh.gk);
+                       (const float *)workspace, y, mn, gk);
     return hipGetLastError();
 }
 
