@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q4_gemv_7b_layer_set_m1-8_traffic.md")
 KERNEL_SOURCES = ("bit_quantized_matmul_q4_amd/csrc/q4_kernels.hip", "bit_quantized_matmul_q4_amd/csrc/q4_device.hpp",
-                  "bit_quantized_matmul_q4_amd/csrc/q4_plan.hpp")
+                  "bit_quantized_matmul_q4_amd/csrc/q4_plan.hpp", "bit_quantized_matmul_q4_amd/build.py")
 
 
 def measured_traffic():
@@ -338,7 +338,7 @@ def main() -> int:
     # ---- GEMV -> GEMM crossover on the layer set
     crossover = None
     if not args.no_crossover:
-        cM = list(range(1, 17)) + [20, 24, 28, 32, 33, 36, 40, 44, 48, 64, 96, 124, 128]
+        cM = list(range(1, 21)) + [24, 28, 32, 33, 36, 40, 44, 48, 64, 96, 124, 128]
         table = []
         for M in cM:
             t = {}
