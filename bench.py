@@ -156,7 +156,7 @@ def main() -> int:
         xs[K] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
     ys = {(mi, M): torch.empty((M, m.N), dtype=torch.float32, device=dev)
           for mi, m in enumerate(mats) for M in range(1, Mmax + 1)
-          if M <= 16 or M in (19, 20, 24, 28, 32, 33, 36, 40, 44, 48, 64, 85, 96, 124, 128)}
+          if M <= 20 or M in (24, 28, 32, 33, 36, 40, 44, 48, 64, 85, 96, 124, 128)}
     torch.cuda.synchronize()
 
     yf = {(j, M): torch.empty((M, fmats[j][0]), dtype=torch.float32, device=dev)
