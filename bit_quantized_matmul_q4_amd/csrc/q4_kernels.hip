@@ -556,14 +556,14 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // refills past the K-group's end fall outside the resources' exact ranges
 // and read nothing), so every weight byte a workgroup needs is loaded once,
 // by the wave that uses it, with many bytes in flight.  The unit's
-// activations, 16 RT rows by 128 k per quad in A-operand lane order (chunk
-// (row tile, block): lane l's 16 bytes at 16 l), arrive in a GW_XS-deep LDS
-// ring by direct global-to-LDS loads spread over the waves; every wave
-// issues RT of them per quad (chunks past the stage go to a 1 KB placeholder
-// target and read nothing), so one immediate vmcnt and one barrier per quad
-// order the ring.  Per block a wave dequantizes its B operand once for its
-// RT row tiles and runs 2 RT block dots (D and the correction E of each row
-// tile).
+// activations, 16 RT rows by 128 k per quad (rows of 256 bytes, granules
+// swizzled; see gemm_ws_a_offset), arrive in a GW_XS-deep LDS ring by
+// direct global-to-LDS loads of four rows each, spread over the waves;
+// every wave issues RT of them per quad (chunks past the stage go to a 1 KB
+// placeholder target and read nothing), so one immediate vmcnt and one
+// barrier per quad order the ring.  Per block a wave dequantizes its B
+// operand once for its RT row tiles and runs 2 RT block dots (D and the
+// correction E of each row tile).
 //
 // The grid is one-dimensional over (column unit, row unit) and K-groups in y:
 // workgroup id -> column unit 8 (id / 8 nru) + id % 8, row unit (id / 8) %
@@ -579,6 +579,18 @@ constexpr int GW_DW = GW_DW_FIXED;
 #else
 constexpr int GW_DW = 4;  // weight ring stages (registers)
 #endif
+
+// The activation stage holds, per row tile, 16 rows of the quad's 256 bytes
+// (4 KB); row c's 16-byte granule j sits at granule j ^ c.  One direct load
+// fills four rows (lane l: row l / 16, granule l % 16 of the LDS row), so
+// every request covers whole cache lines; the swizzle keeps the A-operand
+// reads (lane (g, c): row c, granule 4 i + g of block i) on 16 distinct bank
+// groups.
+__device__ __forceinline__ uint32_t gemm_ws_a_offset(int rt, int i, int lane)
+{
+    const int g = lane >> 4, c = lane & 15;
+    return (uint32_t)(rt * 4096 + c * 256 + 16 * ((4 * i + g) ^ c));
+}
 
 // One quad of a wave's column tile for its RT row tiles: codes w and
 // scales s from the register ring, the A operands from the LDS stage stg.
@@ -598,7 +610,7 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
             u32x4 A[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                A[rt] = *(const u32x4 *)(stg + (rt * 4 + i) * 1024 + 16 * lane);
+                A[rt] = *(const u32x4 *)(stg + gemm_ws_a_offset(rt, i, lane));
             // the block dots first, so they overlap in the matrix pipe
             f32x4 E[RT], Dm[RT];
 #pragma unroll
@@ -665,13 +677,14 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
         uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
         const bool live = qq < nquads;
         const int q = qbeg + qq;
+        const int xr = lane >> 4, xj = lane & 15;  // row in the chunk, LDS granule
 #pragma unroll
         for (int h = 0; h < RT; ++h) {
-            const int ch = w + CT * h;  // chunk = row tile * 4 + block
+            const int ch = w + CT * h;  // chunk = row tile * 4 + group of four rows
             const bool real = ch < NCH;
-            const int rt = ch >> 2, i = ch & 3;
+            const int row = 16 * (ch >> 2) + 4 * (ch & 3) + xr;  // in the unit
             const uint32_t off =
-                live && real ? (uint32_t)(16 * rt + c) * xrow + 256u * q + 64u * i + 16u * g : x_range;
+                live && real ? (uint32_t)row * xrow + 256u * q + 16u * (uint32_t)(xj ^ (row & 15)) : x_range;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(real ? stg + ch * 1024 : xdummy), 16, off, 0,
                                                      0, 0);
         }
