@@ -594,36 +594,63 @@ __device__ __forceinline__ uint32_t gemm_ws_a_offset(int rt, int i, int lane)
 
 // One quad of a wave's column tile for its RT row tiles: codes w and
 // scales s from the register ring, the A operands from the LDS stage stg.
-// (Software-pipelining the blocks, block dots of block i before the
-// scale-accumulate of block i - 1, measured faster only at three and four
-// row tiles, whose units lose to smaller ones; at one or two row tiles its
-// registers cost occupancy.)
+// Few waves share a SIMD and they leave each barrier together, so at one
+// row tile the quad is laid out for latency: every A read first, then every
+// B operand, every block dot, and last the scale-accumulates in block order
+// (block by block, each block paid an LDS round trip and a matrix-core
+// latency in series).  At two row tiles that layout's registers cost more
+// occupancy than it saves, and the blocks go one by one.  Either way each
+// row's blocks accumulate in ascending order.
 template <bool BF16, int RT, bool SHORT>
 __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *stg, int lane, int nq,
                                              const Dequant<BF16> &dq, f32x4 (&p)[RT])
 {
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    auto scale = [&](int i) {
+        const uint32_t sd = i < 2 ? s.x : s.y;
+        return half_bits_to_float((i & 1) ? sd >> 16 : sd & 0xFFFFu);
+    };
+    if constexpr (RT == 1) {
+        u32x4 A[4], B[4];
+        f32x4 E[4], Dm[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!SHORT || i < nq) {
-            const u32x4 B = dq(wd[i]);
-            u32x4 A[RT];
+        for (int i = 0; i < 4; ++i)
+            A[i] = *(const u32x4 *)(stg + gemm_ws_a_offset(0, i, lane));
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                A[rt] = *(const u32x4 *)(stg + gemm_ws_a_offset(rt, i, lane));
-            // the block dots first, so they overlap in the matrix pipe
-            f32x4 E[RT], Dm[RT];
+        for (int i = 0; i < 4; ++i)
+            B[i] = dq(wd[i]);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                E[rt] = blockdot<BF16>(A[rt], dq.offset);
+        for (int i = 0; i < 4; ++i)
+            E[i] = blockdot<BF16>(A[i], dq.offset);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                Dm[rt] = blockdot<BF16>(A[rt], B);
-            const uint32_t sd = i < 2 ? s.x : s.y;
-            const float dsc = half_bits_to_float((i & 1) ? sd >> 16 : sd & 0xFFFFu);
+        for (int i = 0; i < 4; ++i)
+            Dm[i] = blockdot<BF16>(A[i], B[i]);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                scale_accumulate(p[rt], dsc, Dm[rt], E[rt]);
+        for (int i = 0; i < 4; ++i)
+            if (!SHORT || i < nq)  // blocks past a short last quad: not accumulated
+                scale_accumulate(p[0], scale(i), Dm[i], E[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!SHORT || i < nq) {
+                const u32x4 B = dq(wd[i]);
+                u32x4 A[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    A[rt] = *(const u32x4 *)(stg + gemm_ws_a_offset(rt, i, lane));
+                // the block dots first, so they overlap in the matrix pipe
+                f32x4 E[RT], Dm[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    E[rt] = blockdot<BF16>(A[rt], dq.offset);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    Dm[rt] = blockdot<BF16>(A[rt], B);
+                const float dsc = scale(i);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    scale_accumulate(p[rt], dsc, Dm[rt], E[rt]);
+            }
         }
     }
 }
@@ -721,6 +748,12 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
         issue_w(ring[d]);
         issue_fence();
     }
+    // Everything the prologue issued lands before the loop (it went out
+    // together, and the first quad needs its first loads): with loads still
+    // pending from the prologue, the loop header merges two different
+    // histories and the compiler's waits for the weight stages collapse to
+    // "almost everything landed", a memory round trip per quad.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     const Dequant<BF16> dq;
     f32x4 p[RT];
@@ -731,39 +764,48 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     int li = 0;
     int seg_end = ((j0 + 1) * G) >> plan.log2S;
 
-    for (int base = 0; base < nquads; base += GW_DW) {
-#pragma unroll
-        for (int d = 0; d < GW_DW; ++d) {
-            const int qq = base + d;
-            if (qq < nquads) {
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(XWAIT));
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                issue_x(qq + GW_XS - 1);
-                issue_fence();
+    // One quad: stage d of the weight ring, quad qq of the K-group.
+    auto quad = [&](int d, int qq) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(XWAIT));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_x(qq + GW_XS - 1);
+        issue_fence();
 
-                const uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
-                const int q = qbeg + qq;
-                // blocks in the quad: 4, except a short last quad (SHORT only)
-                const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
-                if (live_ct)
-                    gemm_ws_quad<BF16, RT, SHORT>(ring[d].w, ring[d].s, stg, lane, nq, dq, p);
-                if (q + 1 == seg_end) {  // segment j0 + li done
-                    if (!stack.push_branch(p, li, L)) {
+        const uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
+        const int q = qbeg + qq;
+        // blocks in the quad: 4, except a short last quad (SHORT only)
+        const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
+        if (live_ct)
+            gemm_ws_quad<BF16, RT, SHORT>(ring[d].w, ring[d].s, stg, lane, nq, dq, p);
+        if (q + 1 == seg_end) {  // segment j0 + li done
+            if (!stack.push_branch(p, li, L)) {
 #pragma unroll
-                        for (int a = 0; a < RT; ++a)
-                            p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                    }
-                    ++li;
-                    seg_end = ((j0 + li + 1) * G) >> plan.log2S;
-                }
-                issue_fence();
-                issue_w(ring[d]);  // quad qq + GW_DW (past the end: reads nothing)
-                issue_fence();
+                for (int a = 0; a < RT; ++a)
+                    p[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
+            ++li;
+            seg_end = ((j0 + li + 1) * G) >> plan.log2S;
         }
+        issue_fence();
+        issue_w(ring[d]);  // quad qq + GW_DW (past the end: reads nothing)
+        issue_fence();
+    };
+    // Whole rounds of the ring in the loop, the remainder after it: with a
+    // guard on each stage inside the loop, the compiler has to allow for a
+    // round that skips stages and still loops, and its waits for the weight
+    // stages then drain almost every load in flight.
+    int base = 0;
+    for (; base + GW_DW <= nquads; base += GW_DW) {
+#pragma unroll
+        for (int d = 0; d < GW_DW; ++d)
+            quad(d, base + d);
     }
+#pragma unroll
+    for (int d = 0; d < GW_DW - 1; ++d)
+        if (base + d < nquads)
+            quad(d, base + d);
     // the placeholder loads land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -1287,8 +1329,10 @@ static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
     const int rows = (M + sh.nru - 1) / sh.nru;
     sh.RT = (rows + 15) / 16;
     const int tiles = (N + 15) / 16;
+    // four waves (column tiles) per workgroup: measured faster than eight at
+    // M = 17..32 (the barrier holds fewer waves in step) and no slower above
     static const int e_ct = env_knob("Q4_GEMM_CT", 0);
-    sh.CT = e_ct >= 4 && e_ct <= 8 ? e_ct : 8;
+    sh.CT = e_ct >= 4 && e_ct <= 8 ? e_ct : 4;
     sh.ncu = (tiles + sh.CT - 1) / sh.CT;
     sh.gk = 1;
     while (sh.gk < plan.S && (long long)sh.ncu * sh.nru * sh.gk < kComputeUnits &&
