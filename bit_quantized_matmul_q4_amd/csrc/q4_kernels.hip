@@ -493,46 +493,77 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 #pragma unroll
     for (int r = 0; r < R; ++r)
         p[r] = 0.f;
-    for (int base = 0; base < npos; base += D) {
+    // ring position pos (tile pos / LQ, quad d % LQ) from stage d
+    auto compute = [&](int d, int pos) {
+        const int q = d % LQ;
+        const int i = pos / LQ;
+        if (q < len) {
+            const int nq = SHORT && qs + q == G - 1 ? plan.nb - 4 * (G - 1) : 4;
+            gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
+        }
+        if (q == LQ - 1) {  // the tile's segment partial is done
+            float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int q = d % LQ;
-            const int pos = base + d;
-            const int i = pos / LQ;
-            if (pos < npos) {
-                if (q < len) {
-                    const int nq = SHORT && qs + q == G - 1 ? plan.nb - 4 * (G - 1) : 4;
-                    gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
-                }
-                if (q == LQ - 1) {  // the tile's segment partial is done
-                    float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
+            for (int r = 0; r < R; ++r)
+                if (4 * r + g < mrows)
+                    rt[(4 * r + g) * 16 + c] = p[r];
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        if (4 * r + g < mrows)
-                            rt[(4 * r + g) * 16 + c] = p[r];
+            for (int r = 0; r < R; ++r)
+                p[r] = 0.f;
+            if (i % TC == TC - 1 || i == ntiles - 1) {  // chunk done: the tree
+                workgroup_barrier_lds();
+                const int i0 = i - i % TC;
+                const float *rc = roots + ((i / TC) & 1) * TC * 16 * (MR * 16);
+                for (int o = threadIdx.x; o < TC * 256; o += blockDim.x) {
+                    const int k = o >> 8, row = (o >> 4) & 15, col = o & 15;
+                    if (i0 + k <= i && row < mrows) {
+                        float v[16];
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        p[r] = 0.f;
-                    if (i % TC == TC - 1 || i == ntiles - 1) {  // chunk done: the tree
-                        workgroup_barrier_lds();
-                        const int i0 = i - i % TC;
-                        const float *rc = roots + ((i / TC) & 1) * TC * 16 * (MR * 16);
-                        for (int o = threadIdx.x; o < TC * 256; o += blockDim.x) {
-                            const int k = o >> 8, row = (o >> 4) & 15, col = o & 15;
-                            if (i0 + k <= i && row < mrows) {
-                                float v[16];
-#pragma unroll
-                                for (int sg = 0; sg < 16; ++sg)
-                                    v[sg] = rc[(k * 16 + sg) * (MR * 16) + row * 16 + col];
-                                ystage[((i0 + k) * MR + row) * 16 + col] = tree_sum<16>(v, 16);
-                            }
-                        }
+                        for (int sg = 0; sg < 16; ++sg)
+                            v[sg] = rc[(k * 16 + sg) * (MR * 16) + row * 16 + col];
+                        ystage[((i0 + k) * MR + row) * 16 + col] = tree_sum<16>(v, 16);
                     }
                 }
             }
-            issue_fence();
-            load(ring[d], pos + D, q);  // refill D positions ahead (D % LQ == 0: same quad)
-            issue_fence();
+        }
+    };
+    auto refill = [&](int d, int pos) {
+        issue_fence();
+        load(ring[d], pos + D, d % LQ);  // D positions ahead (D % LQ == 0: same quad)
+        issue_fence();
+    };
+    if constexpr (LQ <= 2 && R <= 2) {
+        // Whole rounds of the ring in the loop, the remainder (a multiple of
+        // LQ) after it: with a guard on each stage's compute in the loop, the
+        // compiler has to allow for a round that skips stages and still
+        // loops, and its waits for the ring then drain more of it than the
+        // round needs (measured: gate 11.8 -> 11.5 us at M = 1).
+        int base = 0;
+        for (; base + D <= npos; base += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute(d, base + d);
+                refill(d, base + d);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D - LQ; ++d)
+            if (base + d < npos) {
+                compute(d, base + d);
+                refill(d, base + d);
+            }
+    } else {
+        // three-quad segments or four accumulators: a second copy of the
+        // loop body does not fit the 128 registers of a 1024-thread
+        // workgroup (it spills), so the stages' compute is guarded inside
+        // the loop (the refills past the end read nothing)
+        for (int base = 0; base < npos; base += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (base + d < npos)
+                    compute(d, base + d);
+                refill(d, base + d);
+            }
         }
     }
     __syncthreads();
