@@ -158,3 +158,25 @@ def test_small_workloads_full(workload):
                 y = q4.linear(gu.x_to_dev(x[:M], bf16), w, kernel=kernel).cpu().numpy()
                 err = oracle.max_normalised_error(y, y_ref[:M], a_ref[:M])
                 assert err <= gu.TOL, (mat.name, M, kernel, err)
+
+
+# The matrix-matrix kernel's grid: many row units (M = 300: 19 units of 16
+# rows), column units that do not fill the last group of eight (the spare
+# workgroups return), 32-row units above K = 8192, and K split over 2..16
+# groups with a short last quad; with and without the split workspace.
+GEMM_GRID_SHAPES = [
+    (300, 200, 1024, True), (70, 1000, 9024, False), (33, 4100, 2080, True), (129, 16, 4128, True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,bf16", GEMM_GRID_SHAPES)
+def test_gemm_grid_parity_and_bits(M, N, K, bf16):
+    gu.note("gemm grid M=%d N=%d K=%d bf16=%s" % (M, N, K, bf16))
+    x, codes, s = synth.problem(N, K, M, "bf16" if bf16 else "f16", workload=93, matrix=N * 7 + K)
+    y, _, _ = check(x, bf16, codes, s, "gemm")
+    w = gu.pack_dev(codes, s)
+    xd = gu.x_to_dev(x, bf16)
+    y_plain = q4.linear(xd, w, kernel="gemm", workspace=None).cpu().numpy()  # no K split
+    y_mv = q4.linear(xd, w, kernel="gemv").cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y_plain.view(np.uint32))
+    assert np.array_equal(y.view(np.uint32), y_mv.view(np.uint32))
