@@ -608,7 +608,7 @@ constexpr int GW_XS = 3;  // x ring stages (LDS)
 #ifdef GW_DW_FIXED
 constexpr int GW_DW = GW_DW_FIXED;
 #else
-constexpr int GW_DW = 4;  // weight ring stages (registers)
+constexpr int GW_DW = 6;  // weight ring stages (registers; 6 beat 4 and 8 on gate)
 #endif
 
 // The activation stage holds, per row tile, 16 rows of the quad's 256 bytes
