@@ -576,9 +576,6 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 }
 
 // =================================================================== GEMM
-// s_waitcnt immediate: vmcnt <= n (n < 64), expcnt and lgkmcnt not waited.
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
 // The weight-streaming matrix-matrix kernel.  A workgroup of CT waves
 // (CT = blockDim / 64, 4..8) owns an output unit of 16 RT rows (RT = 1, 2) by
 // CT column tiles and one K-group; wave w computes column tile w of the unit
@@ -588,23 +585,16 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // and read nothing), so every weight byte a workgroup needs is loaded once,
 // by the wave that uses it, with many bytes in flight.  The unit's
 // activations, 16 RT rows by 128 k per quad (rows of 256 bytes, granules
-// swizzled; see gemm_ws_a_offset), arrive in a GW_XS-deep LDS ring by
-// direct global-to-LDS loads of four rows each, spread over the waves;
-// every wave issues RT of them per quad (chunks past the stage go to a 1 KB
-// placeholder target and read nothing), so one immediate vmcnt and one
-// barrier per quad order the ring.  Per block a wave dequantizes its B
-// operand once for its RT row tiles and runs 2 RT block dots (D and the
-// correction E of each row tile).
+// swizzled; see gemm_ws_a_offset), are loaded by the waves in chunks of four
+// rows into registers two quads ahead and written to a two-stage LDS ring
+// one quad ahead; one barrier per quad publishes a stage.  Per block a wave
+// dequantizes its B operand once for its RT row tiles and runs 2 RT block
+// dots (D and the correction E of each row tile).
 //
 // The grid is one-dimensional over (column unit, row unit) and K-groups in y:
 // workgroup id -> column unit 8 (id / 8 nru) + id % 8, row unit (id / 8) %
 // nru, so the row units of one column unit (which read the same weights) are
 // eight ids apart: dispatched together, on the same XCD and its L2.
-#ifdef GW_XS_FIXED
-constexpr int GW_XS = GW_XS_FIXED;
-#else
-constexpr int GW_XS = 3;  // x ring stages (LDS)
-#endif
 #ifdef GW_DW_FIXED
 constexpr int GW_DW = GW_DW_FIXED;
 #else
@@ -612,7 +602,7 @@ constexpr int GW_DW = 6;  // weight ring stages (registers; 6 beat 4 and 8 on ga
 #endif
 
 // The activation stage holds, per row tile, 16 rows of the quad's 256 bytes
-// (4 KB); row c's 16-byte granule j sits at granule j ^ c.  One direct load
+// (4 KB); row c's 16-byte granule j sits at granule j ^ c.  One load
 // fills four rows (lane l: row l / 16, granule l % 16 of the LDS row), so
 // every request covers whole cache lines; the swizzle keeps the A-operand
 // reads (lane (g, c): row c, granule 4 i + g of block i) on 16 distinct bank
@@ -692,11 +682,9 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
                                                   int M, int N, int K, Plan plan, int Gk, int ncu, int nru,
                                                   int write_partial)
 {
-    typedef __attribute__((address_space(3))) void lds_t;
     constexpr int NCH = 4 * RT;  // x chunks per stage
     constexpr int XSTAGE = NCH * 1024;
-    __shared__ __attribute__((aligned(1024))) uint8_t xring[GW_XS * XSTAGE + 1024];
-    uint8_t *const xdummy = xring + GW_XS * XSTAGE;  // the placeholders' target, never read
+    __shared__ __attribute__((aligned(1024))) uint8_t xring[2 * XSTAGE];
 
     const int CT = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -731,20 +719,35 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + tq * 1024, w_range);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + tq * 64, s_range);
 
-    auto issue_x = [&](int qq) {  // quad qq of the K-group into its stage
-        uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
+    // x of quad qq: the wave's chunks (RT of them: chunk w + CT h, four rows
+    // each) into registers, then into LDS stage qq % 2 (lane l's 16 bytes at
+    // 16 l of the chunk).  Chunks past the quads fall outside x's range (zero,
+    // no memory access).
+    const int xr = lane >> 4, xj = lane & 15;  // row in the chunk, LDS granule
+    // x register sets: x is loaded XSETS - 1 quads ahead of its use
+    constexpr int XSETS = RT == 1 ? 6 : 3;
+    u32x4 xreg[XSETS][RT];
+    auto load_x = [&](u32x4 (&xv)[RT], int qq) {
         const bool live = qq < nquads;
         const int q = qbeg + qq;
-        const int xr = lane >> 4, xj = lane & 15;  // row in the chunk, LDS granule
 #pragma unroll
         for (int h = 0; h < RT; ++h) {
             const int ch = w + CT * h;  // chunk = row tile * 4 + group of four rows
-            const bool real = ch < NCH;
-            const int row = 16 * (ch >> 2) + 4 * (ch & 3) + xr;  // in the unit
-            const uint32_t off =
-                live && real ? (uint32_t)row * xrow + 256u * q + 16u * (uint32_t)(xj ^ (row & 15)) : x_range;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_t *)(real ? stg + ch * 1024 : xdummy), 16, off, 0,
-                                                     0, 0);
+            if (ch < NCH) {
+                const int row = 16 * (ch >> 2) + 4 * (ch & 3) + xr;  // in the unit
+                const uint32_t off =
+                    live ? (uint32_t)row * xrow + 256u * q + 16u * (uint32_t)(xj ^ (row & 15)) : x_range;
+                xv[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            }
+        }
+    };
+    auto write_x = [&](const u32x4 (&xv)[RT], int qq) {
+        uint8_t *stg = xring + (qq & 1) * XSTAGE;
+#pragma unroll
+        for (int h = 0; h < RT; ++h) {
+            const int ch = w + CT * h;
+            if (ch < NCH)
+                *(u32x4 *)(stg + ch * 1024 + 16 * lane) = xv[h];
         }
     };
     struct WStage {
@@ -760,25 +763,28 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
         s_off += 128u;
     };
 
-    // Issue order: x stages 0 .. GW_XS - 2, weight stages 0 .. GW_DW - 1;
-    // then per quad t: [wait, barrier] x stage t + GW_XS - 1, compute t,
-    // weight refill t + GW_DW.  Loads issued after x stage t by the top of
-    // quad t: at least the refill of its own quad and GW_XS - 2 quads of both
-    // kinds (more in the prologue), so waiting for that many to remain
-    // outstanding lands x stage t; weight stage t (issued earlier, as
-    // GW_DW > GW_XS - 1) with it.
-    constexpr int XWAIT = 2 + (GW_XS - 2) * (RT + 2);
-    static_assert(GW_DW > GW_XS - 1, "the weight stage must precede its x stage");
+    // x of quad t goes out at quad t - XSETS into register set t % XSETS and
+    // into LDS at quad t - 1; the barrier that opens quad t publishes it.
+    // Loaded several quads before its write, the wait the compiler puts
+    // before the write (it counts conservatively) covers only old loads, so
+    // the weight ring keeps its depth (loaded one quad before, the write
+    // waited for the previous quad's weight refill).  The
+    // weight stages are ordinary register loads the compiler waits for.  No
+    // direct global-to-LDS loads: mixed with register loads on the one
+    // memory counter, an immediate wait did not reliably cover them (stale
+    // activation chunks, measured), and here nothing relies on which loads a
+    // count covers.
+    static_assert(GW_DW % XSETS == 0 && GW_DW % 2 == 0, "register sets and LDS stages by static index");
 #pragma unroll
-    for (int s2 = 0; s2 < GW_XS - 1; ++s2) {
-        issue_x(s2);
-        issue_fence();
-    }
+    for (int k = 0; k < XSETS; ++k)
+        load_x(xreg[k], k);
+    issue_fence();
 #pragma unroll
     for (int d = 0; d < GW_DW; ++d) {
         issue_w(ring[d]);
         issue_fence();
     }
+    write_x(xreg[0], 0);
     // Everything the prologue issued lands before the loop (it went out
     // together, and the first quad needs its first loads): with loads still
     // pending from the prologue, the loop header merges two different
@@ -797,14 +803,11 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
 
     // One quad: stage d of the weight ring, quad qq of the K-group.
     auto quad = [&](int d, int qq) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(XWAIT));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue_x(qq + GW_XS - 1);
+        workgroup_barrier_lds();  // stage qq written, stage qq + 1 free
+        load_x(xreg[d % XSETS], qq + XSETS);
         issue_fence();
 
-        const uint8_t *stg = xring + (qq % GW_XS) * XSTAGE;
+        const uint8_t *stg = xring + (qq & 1) * XSTAGE;
         const int q = qbeg + qq;
         // blocks in the quad: 4, except a short last quad (SHORT only)
         const int nq = SHORT ? min(4, plan.nb - 4 * q) : 4;
@@ -819,6 +822,7 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
             ++li;
             seg_end = ((j0 + li + 1) * G) >> plan.log2S;
         }
+        write_x(xreg[(d + 1) % XSETS], qq + 1);
         issue_fence();
         issue_w(ring[d]);  // quad qq + GW_DW (past the end: reads nothing)
         issue_fence();
@@ -1338,9 +1342,11 @@ static constexpr int kComputeUnits = 256;
 // the units), column units of CT tiles (one wave each), K split over Gk
 // groups when a workspace allows and the grid would otherwise leave compute
 // units idle.  Measured on MI355X (7B shapes, M = 17..124): 16-row units
-// beat 32-, 48- and 64-row ones for K <= 8192 and 32-row units win for
-// K = 18944 (the row units of a column unit read its weights from one L2,
-// and small units keep occupancy up and LDS traffic down).
+// beat 32-, 48- and 64-row ones for K <= 8192 up to M = 64, and 32-row units
+// win for K = 18944 and for wide N above M = 64 (gate at M = 124: 62.6 ->
+// 55.0 us), where sharing each dequantized B operand over two row tiles
+// outweighs the occupancy it costs (the row units of a column unit read its
+// weights from one L2).
 struct GemmWsShape {
     int RT, nru, CT, ncu, gk;
 };
@@ -1350,7 +1356,8 @@ static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
     const Plan plan = make_plan(K);
     GemmWsShape sh;
     static const int e_rt = env_knob("Q4_GEMM_RT", 0);  // for measurement
-    int rt = K > 8192 ? 2 : 1;
+    const int tiles = (N + 15) / 16;
+    int rt = K > 8192 || (M > 64 && tiles >= 1024) ? 2 : 1;
     if (e_rt == 1 || e_rt == 2)
         rt = e_rt;
     // 16 RT rows of x stay below 2^31 bytes (32-bit offsets)
@@ -1359,7 +1366,6 @@ static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
     sh.nru = (M + 16 * rt - 1) / (16 * rt);
     const int rows = (M + sh.nru - 1) / sh.nru;
     sh.RT = (rows + 15) / 16;
-    const int tiles = (N + 15) / 16;
     // four waves (column tiles) per workgroup: measured faster than eight at
     // M = 17..32 (the barrier holds fewer waves in step) and no slower above
     static const int e_ct = env_knob("Q4_GEMM_CT", 0);

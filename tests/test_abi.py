@@ -99,10 +99,13 @@ def test_crossover_get_set(lib):
 
 def test_workspace_bytes(lib):
     assert lib.q4_workspace_bytes(8, 3584, 3584, _lib.Q4_GEMV) == 0
-    ws = lib.q4_workspace_bytes(124, 3584, 3584, _lib.Q4_GEMM)
-    assert ws > 0 and ws % (124 * 3584 * 4) == 0
-    gk = ws // (124 * 3584 * 4)
-    assert gk & (gk - 1) == 0 and gk <= 16
+    # k_proj at 124 rows: too few column units to fill the GPU, split over K
+    ws = lib.q4_workspace_bytes(124, 512, 3584, _lib.Q4_GEMM)
+    assert ws > 0 and ws % (124 * 512 * 4) == 0
+    gk = ws // (124 * 512 * 4)
+    assert gk & (gk - 1) == 0 and 2 <= gk <= 16
+    # gate at 124 rows fills it without a split: no workspace
+    assert lib.q4_workspace_bytes(124, 18944, 3584, _lib.Q4_GEMM) == 0
     assert lib.q4_workspace_bytes(0, 16, 32, _lib.Q4_GEMM) == 0   # bad shape
     assert lib.q4_workspace_bytes(4, 16, 48, _lib.Q4_GEMM) == 0   # bad shape
 

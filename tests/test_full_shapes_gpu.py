@@ -72,3 +72,19 @@ def test_lm_head_sampled():
         sampled_check(x[:M], wq_t, sc_t, mat.K, ys[M], rng)
     for M in (1, 4, 16):
         assert np.array_equal(ys[64][:M].view(np.uint32), ys[M].view(np.uint32))
+
+
+def test_gemm_large_grid_repeatable():
+    """The matrix-matrix kernel on the LM head (thousands of workgroups),
+    repeated: every call's rows are bit-identical to the matrix-vector
+    kernel's.  (An activation stage once raced its loads: a few workgroups
+    per call read stale chunks, different ones each time.)"""
+    mat = synth.LM_HEAD_7B
+    x = synth.activations(64, mat.K, "bf16", workload=5, matrix=7)
+    wq_t, sc_t = synth.packed_weight(mat.N, mat.K, workload=5, matrix=7)
+    xd, w = gu.x_to_dev(x, True), gu.weight_from_tiled(wq_t, sc_t, mat.N, mat.K)
+    ref = q4.linear(xd[:16], w, kernel="gemv").cpu().numpy().view(np.uint32)
+    for M in (17, 20, 33, 64, 17, 20, 33, 64):
+        gu.note("lm_head gemm repeat M=%d" % M)
+        y = q4.linear(xd[:M], w, kernel="gemm").cpu().numpy().view(np.uint32)
+        assert np.array_equal(y[:16], ref), (M, int((y[:16] != ref).sum()))
