@@ -725,7 +725,7 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     // no memory access).
     const int xr = lane >> 4, xj = lane & 15;  // row in the chunk, LDS granule
     // x register sets: x is loaded XSETS - 1 quads ahead of its use
-    constexpr int XSETS = RT == 1 ? 6 : 3;
+    constexpr int XSETS = RT == 1 ? 6 : 3;  // six at two row tiles cost occupancy (measured slower)
     u32x4 xreg[XSETS][RT];
     auto load_x = [&](u32x4 (&xv)[RT], int qq) {
         const bool live = qq < nquads;
