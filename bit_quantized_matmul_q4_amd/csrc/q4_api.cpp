@@ -8,6 +8,7 @@
 // a measured threshold, <= 4 rows -> matrix-vector).  Here the threshold is
 // the crossover measured on MI355X, and because both kernels share one
 // reduction order the choice changes speed only, never the bits.
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
@@ -27,6 +28,12 @@ namespace {
 // kernel needs a second 16-row slice (102 vs 106 us); at 16 the matrix-vector
 // kernel is 10% faster (73 vs 81 us).  T = 16.
 constexpr int kDefaultCrossover = 16;
+// Long K (K > 8192), measured: the matrix-vector kernel's time grows with the
+// rows (down_proj 3584 x 18944: 16.9 us at 9 rows, 23.2 at 16) while the
+// matrix-matrix kernel, split over K, stays near 16 us; from 9 rows on it is
+// faster, provided it gets its split workspace (without it, down_proj takes
+// several times longer).
+constexpr int kLongK = 8192, kLongKCrossover = 8;
 
 thread_local int g_last_hip = 0;
 
@@ -128,13 +135,26 @@ int q4_segments(int K)
     return q4::make_plan(K).S;
 }
 
+// The kernel Q4_AUTO runs: matrix-vector iff M <= T, except that for
+// K > kLongK the matrix-matrix kernel already runs above min(T, 8) rows when
+// it has the workspace it asks for (ws_ok).
+static int auto_kernel(int M, int K, bool ws_ok)
+{
+    if (forced_kernel() != Q4_AUTO)
+        return forced_kernel();
+    const int T = q4_get_crossover();
+    if (M > T)
+        return Q4_GEMM;
+    if (K > kLongK && M > std::min(T, kLongKCrossover) && ws_ok)
+        return Q4_GEMM;
+    return Q4_GEMV;
+}
+
 size_t q4_workspace_bytes(int M, int N, int K, int kernel)
 {
     if (check_shape(M, N, K) != Q4_OK)
         return 0;
-    int k = kernel;
-    if (k == Q4_AUTO)
-        k = forced_kernel() != Q4_AUTO ? forced_kernel() : (M <= q4_get_crossover() ? Q4_GEMV : Q4_GEMM);
+    const int k = kernel == Q4_AUTO ? auto_kernel(M, K, true) : kernel;
     if (k != Q4_GEMM)
         return 0;
     return q4::gemm_workspace_bytes(M, N, K);
@@ -160,9 +180,9 @@ int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
     if (workspace && !aligned(workspace, 256))
         return Q4_ERR_ALIGN;
 
-    int k = kernel;
-    if (k == Q4_AUTO)
-        k = forced_kernel() != Q4_AUTO ? forced_kernel() : (M <= q4_get_crossover() ? Q4_GEMV : Q4_GEMM);
+    const int k = kernel == Q4_AUTO
+                      ? auto_kernel(M, K, workspace_bytes >= q4::gemm_workspace_bytes(M, N, K))
+                      : kernel;
 
     const bool bf16 = x_dtype == Q4_BF16;
     hipStream_t s = (hipStream_t)stream;

@@ -73,7 +73,7 @@ enum q4_status {
 enum q4_dtype { Q4_F16 = 0, Q4_BF16 = 1, Q4_F32 = 2 /* q4_quantize input only */ };
 
 enum q4_kernel {
-    Q4_AUTO = 0, /* matrix-vector kernel if M <= crossover, else matrix-matrix */
+    Q4_AUTO = 0, /* the crossover rule (see q4_get_crossover) picks the kernel */
     Q4_GEMV = 1, /* force the multi-row matrix-vector kernel (any M) */
     Q4_GEMM = 2  /* force the LDS-staged matrix-matrix (MFMA tile) kernel */
 };
@@ -146,10 +146,13 @@ int q4_quantize(const void *w, int w_dtype, uint8_t *codes, void *scales, int N,
 size_t q4_packed_code_bytes(int N, int K);
 size_t q4_packed_scale_bytes(int N, int K);
 
-/* Crossover threshold T: Q4_AUTO uses the matrix-vector kernel iff M <= T.
- * Initialised from the environment variable Q4_CROSSOVER if set, else the
- * measured default.  q4_set_crossover returns Q4_ERR_SHAPE for T < 0.
- * The threshold never changes results, only speed. */
+/* Crossover threshold T: Q4_AUTO uses the matrix-vector kernel iff M <= T,
+ * except that for K > 8192 it uses the matrix-matrix kernel already for
+ * M > min(T, 8) when the call gets the workspace q4_workspace_bytes(M, N, K,
+ * Q4_AUTO) asks for (q4_linear, which has none, then keeps the matrix-vector
+ * kernel).  T is initialised from the environment variable Q4_CROSSOVER if
+ * set, else the measured default.  q4_set_crossover returns Q4_ERR_SHAPE for
+ * T < 0.  The rule never changes results, only speed. */
 int q4_get_crossover(void);
 int q4_set_crossover(int T);
 

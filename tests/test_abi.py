@@ -106,6 +106,24 @@ def test_workspace_bytes(lib):
     assert gk & (gk - 1) == 0 and 2 <= gk <= 16
     # gate at 124 rows fills it without a split: no workspace
     assert lib.q4_workspace_bytes(124, 18944, 3584, _lib.Q4_GEMM) == 0
+
+
+def test_auto_rule_long_k(lib):
+    """Q4_AUTO keeps the matrix-vector kernel up to T rows, except that for
+    K > 8192 the split matrix-matrix kernel takes over above min(T, 8) rows
+    (its workspace is what q4_workspace_bytes reports for Q4_AUTO)."""
+    old = lib.q4_get_crossover()
+    try:
+        assert lib.q4_set_crossover(16) == 0
+        auto, gemm = _lib.Q4_AUTO, _lib.Q4_GEMM
+        assert lib.q4_workspace_bytes(8, 3584, 18944, auto) == 0           # matrix-vector
+        assert lib.q4_workspace_bytes(12, 3584, 18944, auto) == lib.q4_workspace_bytes(12, 3584, 18944, gemm) > 0
+        assert lib.q4_workspace_bytes(12, 3584, 3584, auto) == 0           # short K: matrix-vector up to T
+        assert lib.q4_set_crossover(4) == 0
+        assert lib.q4_workspace_bytes(6, 3584, 18944, auto) > 0            # above min(T, 8)
+        assert lib.q4_workspace_bytes(4, 3584, 18944, auto) == 0
+    finally:
+        lib.q4_set_crossover(old)
     assert lib.q4_workspace_bytes(0, 16, 32, _lib.Q4_GEMM) == 0   # bad shape
     assert lib.q4_workspace_bytes(4, 16, 48, _lib.Q4_GEMM) == 0   # bad shape
 
