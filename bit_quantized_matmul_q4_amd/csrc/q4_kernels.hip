@@ -23,10 +23,10 @@
 //  * q4_gemm_ws: the matrix-matrix kernel for larger M.  A workgroup of
 //    4..8 waves owns an output unit of 16 or 32 rows by one column tile per
 //    wave; each wave streams its tile's codes and scales through a register
-//    ring and reads the unit's activations from an LDS ring filled by direct
-//    global-to-LDS loads.  K may be split across workgroups (one subtree of
-//    segments each) when a workspace is given; q4_tree_combine then joins
-//    the subtree roots in tree order.
+//    ring and reads the unit's activations from a two-stage LDS ring the
+//    waves fill through registers.  K may be split across workgroups (one
+//    subtree of segments each) when a workspace is given; q4_tree_combine
+//    then joins the subtree roots in tree order.
 //
 //  * q4_pack_kernel: canonical codes and scales -> the tiled layout.
 //
@@ -841,7 +841,7 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     for (int d = 0; d < GW_DW - 1; ++d)
         if (base + d < nquads)
             quad(d, base + d);
-    // the placeholder loads land before the workgroup's LDS is released
+    // the refills past the end (they read nothing) land before the wave ends
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // p holds the K-group's subtree roots
