@@ -345,10 +345,17 @@ def main() -> int:
             for kernel in ("gemv", "gemm"):
                 g = capture(lambda M=M, kernel=kernel: [call(mi, M, p % P, kernel)
                                                         for p in range(4) for mi in range(len(mats))])
-                t[kernel] = time_graphs([g], 3) / 4 * 1e3  # us per layer set
+                g.replay()  # untimed first replay
+                # best of three timings: a single disturbed timing must not move M*
+                t[kernel] = min(time_graphs([g], 3) for _ in range(3)) / 4 * 1e3  # us per layer set
             table.append({"M": M, "gemv_us": round(t["gemv"], 2), "gemm_us": round(t["gemm"], 2),
                           "gemm_over_gemv": round(t["gemm"] / t["gemv"], 3)})
-        mstar = next((r["M"] for r in table if r["gemm_us"] < r["gemv_us"]), None)
+        # M*: the first sampled M from which the matrix-matrix kernel stays faster
+        mstar = None
+        for r in reversed(table):
+            if r["gemm_us"] >= r["gemv_us"]:
+                break
+            mstar = r["M"]
         crossover = {"layer_set_table": table, "M_star": mstar,
                      "T_rule": (mstar - 1) if mstar else None,
                      "library_T": q4.get_crossover()}
