@@ -5,8 +5,9 @@ Workload: the Qwen2.5-7B-shaped projection set (q 3584x3584, k and v
 512x3584, gate and up 18944x3584, down 3584x18944), Q4 weights (blocks of 32,
 fp16 scales), bf16 activations, at every decode row count M = 1..8.  One
 step = the six projections at each M = 1..8 (48 calls through the library's
-crossover dispatcher), on a weight copy taken from a rotation pool larger than
-the 256 MB Infinity Cache, so weights stream from HBM.  Inputs are seeded
+crossover dispatcher), each M on its own weight copy taken from a rotation
+pool larger than the 256 MB Infinity Cache, so weights stream from HBM (no
+copy is read twice within 1.5 GiB of weight traffic).  Inputs are seeded
 synthetic data of those shapes (no trained weights); every input is resident
 in HBM before the timed region.
 
@@ -17,7 +18,7 @@ host as a baseline.  The GEMV->GEMM crossover on the layer set and the
 per-M bandwidth are reported under "detail".
 
 Timing: each step's 48 launches are captured once in a HIP graph (one graph
-per pool copy); the timed region replays them between two events on the
+per offset into the pool); the timed region replays them between two events on the
 launch stream, after a barrier-free torch.cuda.synchronize() on both sides.
 """
 from __future__ import annotations
@@ -77,6 +78,8 @@ def parse():
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-launch step")
     ap.add_argument("--no-schemes", action="store_true", help="skip the pages' switching schemes comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-per-launch", action="store_true",
+                    help="skip the per-matrix launch timings (per-M and per-matrix GB/s)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--detail-json", default=None, help="also write the full results here")
@@ -203,9 +206,16 @@ def main() -> int:
             % (args.eager_reps, len(eMs) * len(mats), step_bytes(eMs), flops))
         return 0
 
-    # ---- the step: 6 projections x M = 1..8, one graph per pool copy
+    # ---- the step: 6 projections x M = 1..8, one graph per pool offset.
+    # Row count j of step graph p reads copy (p * 8 + j) mod P: each M reads
+    # a copy of its own, so no weight is reread out of the Infinity Cache
+    # (one copy for all eight M would reread it seven times within 1 GB).
+    def copy_of(p, j):
+        return (p * len(Ms) + j) % P
+
     log("capturing %d step graphs" % P)
-    step_graphs = [capture(lambda p=p: [call(mi, M, p, args.kernel) for M in Ms for mi in range(len(mats))])
+    step_graphs = [capture(lambda p=p: [call(mi, M, copy_of(p, j), args.kernel)
+                                        for j, M in enumerate(Ms) for mi in range(len(mats))])
                    for p in range(P)]
     for i in range(args.warmup):
         step_graphs[i % P].replay()
@@ -216,31 +226,54 @@ def main() -> int:
     value = bytes_step / (ms_step * 1e-3) / 1e9
     rows_per_s = sum(Ms) / (ms_step * 1e-3)
     log("step %.3f us, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms_step * 1e3, value, 100 * value / PEAK_HBM_GBS))
+    # roofline of the dominant kernel: every launch of the step runs the
+    # matrix-vector kernel, so its average launch duration over the timed
+    # region is the step time over the 48 launches (inter-launch gaps
+    # inside the graph included)
+    n_launch = len(Ms) * len(mats)
+    launch_ms = ms_step / n_launch
+    achieved = bytes_step / n_launch / (launch_ms * 1e-3) / 1e9
 
-    # ---- per-launch durations of the dominant kernel (back-to-back launches
-    # of one shape over the pool, one graph) and per-M bandwidth
+    # ---- per-launch durations of the dominant kernel and per-M bandwidth:
+    # back-to-back launches of one shape, one graph, each launch on another
+    # copy of the matrix.  The copies span at least the pool's size per
+    # matrix (the step pool's copies plus clones), so that every launch
+    # streams its weights from HBM: the step pool alone holds 14 copies of
+    # q_proj (100 MB), which the Infinity Cache would keep.
     per_launch = {}
-    for M in Ms:
-        for mi in range(len(mats)):
-            g = capture(lambda M=M, mi=mi: [call(mi, M, p, args.kernel) for p in range(P)])
-            per_launch[(mi, M)] = time_graphs([g], 3) / P  # ms per launch
-    kern_ms = sum(per_launch.values())
-    achieved = bytes_step / (kern_ms * 1e-3) / 1e9
-    per_m = {}
-    for M in Ms:
-        t = sum(per_launch[(mi, M)] for mi in range(len(mats)))
-        per_m[str(M)] = round(step_bytes([M]) / (t * 1e-3) / 1e9, 1)
-    per_matrix_m8 = {mats[mi].name: round(synth.algorithmic_bytes(8, mats[mi].N, mats[mi].K)
-                                          / (per_launch[(mi, 8)] * 1e-3) / 1e9, 1) for mi in range(len(mats))}
-    log("per-M GB/s %s" % per_m)
-    log("per-matrix GB/s at M=8 %s" % per_matrix_m8)
+    per_m = per_matrix_m8 = per_launch_us = None
+    if not args.no_per_launch:
+        pool_bytes = args.pool_gib * (1 << 30)
+        for mi, m in enumerate(mats):
+            wbytes = sum(q4.packed_sizes(m.N, m.K))
+            extra = [q4.Q4Weight(base[mi].codes.clone(), base[mi].scales.clone(), m.N, m.K)
+                     for _ in range(max(0, int(np.ceil(pool_bytes / wbytes)) - P))]
+            mpool = [pool[p][mi] for p in range(P)] + extra
+            for M in Ms:
+                g = capture(lambda M=M, mi=mi, mpool=mpool: [q4.linear(xs[m.K][:M], w, out=ys[(mi, M)],
+                                                                       kernel=args.kernel) for w in mpool])
+                per_launch[(mi, M)] = time_graphs([g], 3) / len(mpool)  # ms per launch
+                del g
+            del extra, mpool
+            torch.cuda.empty_cache()
+        per_m = {}
+        for M in Ms:
+            t = sum(per_launch[(mi, M)] for mi in range(len(mats)))
+            per_m[str(M)] = round(step_bytes([M]) / (t * 1e-3) / 1e9, 1)
+        per_matrix_m8 = {mats[mi].name: round(synth.algorithmic_bytes(8, mats[mi].N, mats[mi].K)
+                                              / (per_launch[(mi, 8)] * 1e-3) / 1e9, 1) for mi in range(len(mats))}
+        per_launch_us = {m.name: {str(M): round(per_launch[(mi, M)] * 1e3, 2) for M in Ms}
+                         for mi, m in enumerate(mats)}
+        log("per-M GB/s %s" % per_m)
+        log("per-matrix GB/s at M=8 %s" % per_matrix_m8)
 
     # ---- the same step with fused launches: q|k|v (N = 4608) and gate|up
     # (N = 37888) as one call each, down on its own (24 calls); x is read
     # once per fused call, so the step's algorithmic bytes are a little lower
     fused_step = None
     if not args.no_fused:
-        fgraphs = [capture(lambda p=p: [call_fused(j, M, fpool[p][j]) for M in Ms for j in range(len(fmats))])
+        fgraphs = [capture(lambda p=p: [call_fused(j, M, fpool[copy_of(p, i)][j])
+                                        for i, M in enumerate(Ms) for j in range(len(fmats))])
                    for p in range(P)]
         for i in range(args.warmup):
             fgraphs[i % P].replay()
@@ -413,11 +446,11 @@ def main() -> int:
                    "rows_per_s": round(rows_per_s, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "q4_gemv (split and segment forms), bf16", "launches_per_step": len(Ms) * len(mats),
-                     "avg_bytes_per_launch": int(bytes_step / (len(Ms) * len(mats))),
-                     "avg_launch_us": round(kern_ms / (len(Ms) * len(mats)) * 1e3, 3)},
+                     "kernel": "q4_gemv (split and segment forms), bf16", "launches_per_step": n_launch,
+                     "avg_bytes_per_launch": int(bytes_step / n_launch),
+                     "avg_launch_us": round(launch_ms * 1e3, 3)},
         "cpu_baseline": cpu,
-        "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "fused_step": fused_step,
+        "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "per_launch_us": per_launch_us, "fused_step": fused_step,
                    "decode_stream_7b": stream, "switching_schemes": schemes, "crossover": crossover},
     }
     line = json.dumps(out)

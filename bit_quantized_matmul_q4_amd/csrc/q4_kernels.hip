@@ -52,6 +52,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Cache policy of the code and scale loads: the non-temporal hint (nt), for
+// data a call reads once (or, in the matrix-matrix kernel, once per row
+// unit).  Measured on MI355X against the default policy in back-to-back
+// calls: the matrix-vector kernels get 5-9% faster per launch on every
+// 7B-shaped projection at one to eight rows (k_proj 4.87 -> 4.52 us, gate
+// 11.5 -> 10.9 us, down 10.9 -> 9.9 us at one row), the matrix-matrix
+// kernel 0.5 us faster on q_proj and k_proj and unchanged on the larger
+// matrices.  x keeps the default: every workgroup rereads it from L2.
+constexpr int kWeightLoadPolicy = 2;
+
 // One ring stage: one tile-quad of the wave's stream as loaded.  Lane (g, c)
 // holds the B-operand dwords of the quad's four block dots, its column's four
 // scales and its A-operand slice (row slot c, k-slots 8g..8g+7) of the four
@@ -118,8 +128,8 @@ __device__ __forceinline__ void issue_fence()
 template <bool XL>
 __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
-    st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane, in.w_off, 0));
-    st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane, in.s_off, 0));
+    st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane, in.w_off, kWeightLoadPolicy));
+    st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane, in.s_off, kWeightLoadPolicy));
     if constexpr (!XL) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -478,8 +488,8 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         const bool live = q < len && pos < npos;
         const uint32_t wo = live ? (uint32_t)i * tile_b + 1024u * (qs + q) : w_range;
         const uint32_t so = live ? (uint32_t)i * tile_s + 128u * (qs + q) : s_range;
-        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, wo, 0));
-        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane, so, 0));
+        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, wo, kWeightLoadPolicy));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane, so, kWeightLoadPolicy));
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -757,8 +767,8 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     WStage ring[GW_DW];
     uint32_t w_off = 0, s_off = 0;
     auto issue_w = [&](WStage &st) {
-        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane, w_off, 0));
-        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 8u * c, s_off, 0));
+        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane, w_off, kWeightLoadPolicy));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 8u * c, s_off, kWeightLoadPolicy));
         w_off += 1024u;
         s_off += 128u;
     };
