@@ -1111,9 +1111,12 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     const size_t xbytes = rows * gemv_xrow_bytes(K) + 256;
     const size_t roots = sh.split ? 0 : (size_t)4 * sh.tps * 256 * sizeof(float);
     const bool fits = roots + xbytes <= GEMV_XLDS_MAX;
-    // measured: staged x pays for up to 4 rows on wide or long-K matrices;
-    // beyond that its LDS footprint caps the waves a compute unit can hold
-    sh.xl = fits && M <= 4 && (tiles >= 1024 || K >= 8192);
+    // measured on MI355X, weights streaming from HBM: staged x pays for up
+    // to 4 rows (896 x 4864 6.6 -> 5.0 us, 4096 x 4096 6.1 -> 5.4 us,
+    // k_proj 4.5 -> 4.3 us, within 2% elsewhere); from 5 rows on its LDS
+    // footprint caps the waves a compute unit can hold (q_proj at 8 rows
+    // 5.4 -> 5.6 us)
+    sh.xl = fits && M <= 4;
     if (e_xl == 0 || e_xl == 1)
         sh.xl = e_xl == 1 && fits;
     static const int e_tw = env_knob("Q4_GEMV_TW", 0);
