@@ -406,10 +406,15 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // segment's length are placeholders: their loads fall outside the
 // resources' ranges (zero, no memory access) and they compute nothing.
 // grid = (ceil(tiles / tpw), ceil(M / 16)), block = 1024.  With MR =
-// min(M, 16), dynamic LDS: roots [2][TC][16 seg][MR][16] floats, then
-// outputs [tpw][MR][16] floats.
-// TC: tiles per combine (2; 1 above 8 rows, where the partials take 4 KB a row)
-static inline int seg_tc(int M) { return M > 8 ? 1 : 2; }
+// min(M, 16), dynamic LDS: roots [NB][TC][16 seg][MR][16] floats (NB = 1
+// if tpw <= TC: one combine after the last tile; else 2, double-buffered),
+// then outputs [tpw][MR][16] floats.
+// TC: tiles per combine.  Measured on MI355X: with up to 8 tiles per
+// workgroup one combine at the end is fastest (gate at one row 10.7 ->
+// 10.4 us); with more tiles (gate|up, the LM head) combining every 2 tiles
+// is, and above 8 rows 1 (the partials take 4 KB a row).
+__host__ __device__ inline int seg_tc(int M, int tpw) { return M > 8 ? 1 : tpw <= 8 ? 8 : 2; }
+__host__ __device__ inline int seg_nbuf(int tc, int tpw) { return tpw <= tc ? 1 : 2; }
 // Ring depth of the segment form (a multiple of LQ).  Measured on MI355X:
 // 4 stages beat 6, 8 and 10 (a deep per-wave prefetch delays the data each
 // wave needs first and scatters the workgroup's accesses; 2 helps at one row
@@ -444,8 +449,8 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     static_assert(D % LQ == 0, "ring positions must map to fixed quads");
     extern __shared__ __attribute__((aligned(16))) float seg_lds[];
     const int MR = min(M, 16);
-    float *roots = seg_lds;                        // [2][TC][16 seg][MR][16]
-    float *ystage = seg_lds + 2 * TC * 16 * MR * 16;  // [tpw][MR][16]
+    float *roots = seg_lds;                                         // [NB][TC][16 seg][MR][16]
+    float *ystage = seg_lds + seg_nbuf(TC, tpw) * TC * 16 * MR * 16;  // [tpw][MR][16]
 
     const int lane = threadIdx.x & 63;
     const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // segment
@@ -1231,8 +1236,11 @@ template <bool BF16, int R, int LQ>
 static void launch_seg_v(const GemvArgs &a)
 {
     if constexpr (R == 4) {
-        if (seg_tc(a.M) == 1)
+        if (seg_tc(a.M, a.tps) == 1)
             return launch_seg_t<BF16, R, LQ, 1>(a);
+    } else {
+        if (seg_tc(a.M, a.tps) == 8)
+            return launch_seg_t<BF16, R, LQ, 8>(a);
     }
     launch_seg_t<BF16, R, LQ, 2>(a);
 }
@@ -1279,7 +1287,8 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
         return false;
     tpw = e_tpw > 0 ? e_tpw : (tiles + 255) / 256;
     const int MR = M < 16 ? M : 16;
-    lds = (size_t)64 * MR * (2 * seg_tc(M) * 16 + tpw);
+    const int tc = seg_tc(M, tpw);
+    lds = (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw);
     return lds <= SEG_LDS_MAX;
 }
 
