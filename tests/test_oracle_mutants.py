@@ -26,7 +26,10 @@ MUTANTS = {
     "tiled_lane_order": ("16 * (16 * g + c)", "16 * (4 * c + g)"),
     "tiled_word_endian": ("((uint32_t)wq[4 * w + 3] << 24)", "((uint32_t)wq[4 * w + 3] << 16)"),
     "tiled_scale_order": ("* 64 + 4 * c + i", "* 64 + 16 * i + c"),
-    "tiled_quad_stride": ("(t * quads_of(K) + q) * 1024", "(q * ((n + 15) / 16 + 1) + t) * 1024"),
+    # quads per tile rounded down instead of up: tiles overlap when K is not
+    # a multiple of 128 (every index stays inside the buffers, so the
+    # mutant's packer cannot write past them and corrupt the test process)
+    "tiled_quad_stride": ("(t * quads_of(K) + q) * 1024", "(t * (K / 128) + q) * 1024"),
     "offset_7": ("(double)(q - 8)", "(double)(q - 7)"),
     "scale_index": (": scales[n * (K / 32) + k / 32]", ": scales[n * (K / 32) + (k / 32 + 1) % (K / 32)]"),
     "scale_per_16": (": scales[n * (K / 32) + k / 32]", ": scales[n * (K / 32) + (k / 16) % (K / 32)]"),
