@@ -110,8 +110,24 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
 struct GemvStream {
     __amdgpu_buffer_rsrc_t w, s, x;
     uint32_t w_lane, s_lane, x_lane;  // per-lane byte offsets
+    uint32_t xw_lane[2];              // XM_WAVE: rows g and 4 + g, chunk c
     uint32_t w_off, s_off;            // scalar offsets of the next refill
 };
+
+// Where the matrix-vector kernel's A operands (x) come from.
+//  XM_RING: loaded with each ring stage in the A-operand layout: four
+//    16-byte loads a lane (one per block), whatever the row count.
+//  XM_LDS: the workgroup's rows copied into LDS once, before the loop.
+//  XM_WAVE: loaded with each ring stage in row order, 256 contiguous bytes a
+//    row (one 16-byte load a lane per four rows: R loads), and turned into
+//    the A-operand layout through a per-wave LDS slot.  The loads a stage
+//    issues, not their bytes, bound the stream: measured on MI355X, down_proj
+//    at eight rows takes 16.0 us with four x loads a stage and 10.5 us with
+//    one (a timing-only copy).
+enum : int { XM_RING = 0, XM_LDS = 1, XM_WAVE = 2 };
+// Bytes of a row in an XM_WAVE slot: 256 and 16 of padding, so that rows
+// start in different banks.
+constexpr uint32_t XW_ROW = 272;
 
 // Keeps the ring's loads in program order relative to their uses: the empty
 // statement (no instructions) with a memory clobber stops IR-level motion,
@@ -123,18 +139,24 @@ __device__ __forceinline__ void issue_fence()
 }
 
 // Loads one stage: the next quad of the stream and, unless x is staged in
-// LDS (XL), the x blocks of quad x_off / 256 (x_off >= the slice size for a
-// refill past the stream's end).
-template <bool XL>
+// LDS (XM_LDS), the x of quad x_off / 256 (x_off >= the slice size for a
+// refill past the stream's end): the four A-operand blocks (XM_RING) or NW
+// loads of four rows each (XM_WAVE, into xa[0 .. NW - 1]).
+template <int XM, int NW>
 __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
     st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane, in.w_off, kWeightLoadPolicy));
     st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane, in.s_off, kWeightLoadPolicy));
-    if constexpr (!XL) {
+    if constexpr (XM == XM_RING) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b, x_off, 0));
+    } else if constexpr (XM == XM_WAVE) {
+        static_assert(NW == 1 || NW == 2, "XM_WAVE holds up to 8 rows");
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j], x_off, 0));
     }
     in.w_off += 1024;
     in.s_off += 128;
@@ -147,6 +169,23 @@ __device__ __forceinline__ void gemv_x_lds(u32x4 (&xa)[4], const uint8_t *xrow, 
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         xa[b] = *(const u32x4 *)(xrow + 256 * q + 64 * b);
+}
+
+// XM_WAVE: the stage's rows (lane (g, c) of load j holds chunk c of row
+// 4 j + g) through the wave's LDS slot into the A-operand layout (lane (g, c)
+// reads row slot c's k-slots 8g..8g+7 of each block).  wput: the lane's
+// chunk of load 0 in the slot; xget: its A row in the slot, 16 g added.
+// LDS operations of one wave complete in order, so the reads see the writes
+// and the next stage's writes cannot overtake them.
+template <int NW>
+__device__ __forceinline__ void gemv_x_wave(u32x4 (&xa)[4], const GemvStage &st, uint8_t *wput, const uint8_t *xget)
+{
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+        *(u32x4 *)(wput + 4 * XW_ROW * j) = st.xa[j];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        xa[b] = *(const u32x4 *)(xget + 64 * b);
 }
 
 // Row slots of a 16-row slice.  Batch row m sits in A-operand row slot
@@ -169,20 +208,18 @@ __host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t
 //    column tiles, wave (slot, run) streams run `run` (segments run L ..
 //    run L + L - 1) of tile slot `slot`; each tile's W run roots meet in LDS
 //    for the top of the pairwise tree.
-//  XL: the workgroup first copies its x rows into LDS and every wave reads its
-//    A operands there; otherwise each stage loads them with the weights.
-//    Every wave of every workgroup reads the same few kilobytes of x, so as
-//    per-quad loads they become a stream of requests to the same few cache
-//    lines, which costs as much as the weights themselves.
+//  XM (see XM_RING, XM_LDS, XM_WAVE): where the A operands come from.
 // Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
-// (XL) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of slack.
-template <bool BF16, int R, int D, bool SHORT, bool SPLIT, bool XL>
+// (XM_LDS) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of
+// slack, or (XM_WAVE) one slot of 4 R rows of XW_ROW bytes per wave.
+template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x,
                                                               const uint8_t *__restrict__ wq,
                                                               const uint16_t *__restrict__ scales,
                                                               float *__restrict__ y, int M, int N, int K,
                                                               Plan plan, int L, int tps)
 {
+    constexpr bool XL = XM == XM_LDS;
     // SPLIT: the run roots, [wave][row slot][column slot (17)].  Otherwise the
     // stream's tile roots (dynamic LDS): a store inside the streaming loop
     // would make every wait on the ring drain the whole ring (loads and
@@ -233,6 +270,14 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     // rows that are never stored
     const int xr = slot_row(c);  // the batch row of A row slot c
     in.x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        in.xw_lane[j] = 4 * j + g < mrows ? (uint32_t)(4 * j + g) * (uint32_t)K * 2u + 16u * c : x_bytes;
+    // XM_WAVE: the wave's slot; A rows past the batch read the last row
+    // (their outputs are never stored)
+    uint8_t *const wslot = xlds + (uint32_t)wave * (4u * R * XW_ROW);
+    uint8_t *const wput = wslot + (uint32_t)g * XW_ROW + 16u * c;
+    const uint8_t *const xget = wslot + (uint32_t)min(xr, mrows - 1) * XW_ROW + 16u * g;
     in.w_off = 0;
     in.s_off = 0;
 
@@ -272,7 +317,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     int left = total;  // loads left that the stream uses
 #pragma unroll
     for (int d = 0; d < D; ++d) {  // in stage order (see the refill below)
-        gemv_load<XL>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+        gemv_load<XM, R>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
         ql = ql + 1 == q1 ? q0 : ql + 1;
         --left;
         issue_fence();
@@ -315,8 +360,14 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
                 const int qn = qc + 1 == q1 ? q0 : qc + 1;
                 if constexpr (XL)
                     gemv_x_lds(xb[(d + 1) & 1], xrow, qn);
-                gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
-                                          SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                if constexpr (XM == XM_WAVE) {
+                    u32x4 xa[4];
+                    gemv_x_wave<R>(xa, ring[d], wput, xget);
+                    gemv_quad<BF16, R, SHORT>(ring[d], xa, SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                } else {
+                    gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
+                                              SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                }
                 if (qc + 1 == seg_end) {  // segment done: fold into the run's subtree
                     if (stack.push(p, li, L)) {
                         if constexpr (SPLIT) {
@@ -348,7 +399,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             // ranges: they return zero without a memory access, so the
             // wave's end does not wait one more round trip for them.
             issue_fence();
-            gemv_load<XL>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+            gemv_load<XM, R>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
             ql = ql + 1 == q1 ? q0 : ql + 1;
             --left;
             issue_fence();
@@ -1063,7 +1114,8 @@ static int env_knob(const char *name, int dflt)
 }
 
 struct GemvShape {
-    bool split, xl;
+    bool split;
+    int xm;  // XM_RING, XM_LDS or XM_WAVE
     int L, tps, D, tw;  // tw: column tiles per split workgroup
     size_t lds;  // dynamic LDS bytes
 };
@@ -1121,16 +1173,28 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     // k_proj 4.5 -> 4.3 us, within 2% elsewhere); from 5 rows on its LDS
     // footprint caps the waves a compute unit can hold (q_proj at 8 rows
     // 5.4 -> 5.6 us)
-    sh.xl = fits && M <= 4;
-    if (e_xl == 0 || e_xl == 1)
-        sh.xl = e_xl == 1 && fits;
+    sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
+    // measured on MI355X: with eight runs a tile (K = 4096, 4864, 8192,
+    // 18944) x through per-wave slots beats both up to 8 rows (down_proj at
+    // 4 / 8 rows 11.9 / 15.8 -> 10.6 / 13.3 us, 4096 x 4096 5.4 / 6.4 -> 5.0 /
+    // 5.7 us); with fewer, longer runs (K = 896, 3584) it is 1-9% slower
+    if (sh.split && plan.S / sh.L == 8 && M <= 8)
+        sh.xm = XM_WAVE;
+    // Q4_GEMV_XLDS (measurement): 0 = x through the ring, 1 = staged in LDS
+    // (if it fits), 2 = through per-wave LDS slots (up to 8 rows)
+    if (e_xl == 0 || e_xl == 2)
+        sh.xm = e_xl == 2 && M <= 8 ? XM_WAVE : XM_RING;
+    if (e_xl == 1)
+        sh.xm = fits ? XM_LDS : XM_RING;
     static const int e_tw = env_knob("Q4_GEMV_TW", 0);
     sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
     if (e_tw == 1 || e_tw == 2 || e_tw == 4)
-        sh.tw = sh.split && sh.xl && e_tw * (plan.S / sh.L) <= 8 ? e_tw : 1;
-    if (!sh.xl && sh.split)
-        sh.D = 4;  // x rides in the ring: 22 registers a stage
-    sh.lds = roots + (sh.xl ? xbytes : 0);
+        sh.tw = sh.split && sh.xm == XM_LDS && e_tw * (plan.S / sh.L) <= 8 ? e_tw : 1;
+    if (sh.xm != XM_LDS && sh.split)
+        sh.D = 4;  // x rides in the ring: up to 22 registers a stage
+    const int waves = sh.split ? (plan.S / sh.L) * sh.tw : 4;
+    const size_t wslots = (size_t)waves * 4 * (rows <= 4 ? 1 : 2) * XW_ROW;
+    sh.lds = roots + (sh.xm == XM_LDS ? xbytes : sh.xm == XM_WAVE ? wslots : 0);
     return sh;
 }
 
@@ -1146,10 +1210,10 @@ struct GemvArgs {
     Plan plan;
 };
 
-template <bool BF16, int R, int D, bool SPLIT, bool XL>
+template <bool BF16, int R, int D, bool SPLIT, int XL>
 static void launch_gemv_v(const GemvArgs &a)
 {
-    if constexpr (XL) {
+    if constexpr (XL == XM_LDS) {
         static const bool lds_raised = [] {
             // a failure here leaves the default limit; the launch then reports it
             (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL>,
@@ -1168,31 +1232,48 @@ static void launch_gemv_v(const GemvArgs &a)
                            a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
 }
 
-// Built variants: x in LDS with a 4-deep ring; x in the ring with a 4-deep
-// (split) or 4/8-deep (one stream per wave) ring.
+// Built variants: x in LDS with a 4-deep ring; x through per-wave slots
+// (up to 8 rows) with a 4-deep ring; x in the ring with a 4-deep (split) or
+// 4/8-deep (one stream per wave) ring.
 template <bool BF16, int R>
 static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
 {
-    if (sh.xl) {
+    if (sh.xm == XM_LDS) {
 #ifdef GEMV_XL_DEPTH
         constexpr int DX = GEMV_XL_DEPTH;
 #else
         constexpr int DX = 4;  // measured: 4 beats 6 and 8 (down_proj, M <= 4)
 #endif
         if (sh.split)
-            launch_gemv_v<BF16, R, DX, true, true>(a);
+            launch_gemv_v<BF16, R, DX, true, XM_LDS>(a);
         else
-            launch_gemv_v<BF16, R, DX, false, true>(a);
-    } else if (sh.split) {
-#ifdef GEMV_SPLIT_DEPTH
-        launch_gemv_v<BF16, R, GEMV_SPLIT_DEPTH, true, false>(a);
+            launch_gemv_v<BF16, R, DX, false, XM_LDS>(a);
+        return;
+    }
+    if constexpr (R <= 2) {
+        if (sh.xm == XM_WAVE) {
+#ifdef GEMV_WAVE_DEPTH
+            constexpr int DW = GEMV_WAVE_DEPTH;
 #else
-        launch_gemv_v<BF16, R, 4, true, false>(a);
+            constexpr int DW = 4;
+#endif
+            if (sh.split)
+                launch_gemv_v<BF16, R, DW, true, XM_WAVE>(a);
+            else
+                launch_gemv_v<BF16, R, DW, false, XM_WAVE>(a);
+            return;
+        }
+    }
+    if (sh.split) {
+#ifdef GEMV_SPLIT_DEPTH
+        launch_gemv_v<BF16, R, GEMV_SPLIT_DEPTH, true, XM_RING>(a);
+#else
+        launch_gemv_v<BF16, R, 4, true, XM_RING>(a);
 #endif
     } else if (sh.D == 4) {
-        launch_gemv_v<BF16, R, 4, false, false>(a);
+        launch_gemv_v<BF16, R, 4, false, XM_RING>(a);
     } else {
-        launch_gemv_v<BF16, R, 8, false, false>(a);
+        launch_gemv_v<BF16, R, 8, false, XM_RING>(a);
     }
 }
 
