@@ -120,10 +120,11 @@ struct GemvStream {
 //  XM_LDS: the workgroup's rows copied into LDS once, before the loop.
 //  XM_WAVE: loaded with each ring stage in row order, 256 contiguous bytes a
 //    row (one 16-byte load a lane per four rows: R loads), and turned into
-//    the A-operand layout through a per-wave LDS slot.  The loads a stage
-//    issues, not their bytes, bound the stream: measured on MI355X, down_proj
-//    at eight rows takes 16.0 us with four x loads a stage and 10.5 us with
-//    one (a timing-only copy).
+//    the A-operand layout through a per-wave LDS slot.  The cache lines x's
+//    loads request per stage bound these streams: at eight rows XM_RING
+//    requests 32 a stage (each load touches 64 bytes of 8 rows) and XM_WAVE
+//    16 (each line once); measured on MI355X, down_proj at eight rows takes
+//    16.0 us and 13.3 us.
 enum : int { XM_RING = 0, XM_LDS = 1, XM_WAVE = 2 };
 // Bytes of a row in an XM_WAVE slot: 256 and 16 of padding, so that rows
 // start in different banks.
