@@ -125,7 +125,11 @@ struct GemvStream {
 //    requests 32 a stage (each load touches 64 bytes of 8 rows) and XM_WAVE
 //    16 (each line once); measured on MI355X, down_proj at eight rows takes
 //    16.0 us and 13.3 us.
-enum : int { XM_RING = 0, XM_LDS = 1, XM_WAVE = 2 };
+//  XM_QUAD: up to 8 rows, loaded with each ring stage into the A-operand
+//    layout by the lanes of the unused row slots as well, so that each load
+//    reads whole 128-byte lines of its rows, then moved within each quad of
+//    lanes by DPP (no LDS).
+enum : int { XM_RING = 0, XM_LDS = 1, XM_WAVE = 2, XM_QUAD = 3 };
 // Bytes of a row in an XM_WAVE slot: 256 and 16 of padding, so that rows
 // start in different banks.
 constexpr uint32_t XW_ROW = 272;
@@ -153,8 +157,8 @@ __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b, x_off, 0));
-    } else if constexpr (XM == XM_WAVE) {
-        static_assert(NW == 1 || NW == 2, "XM_WAVE holds up to 8 rows");
+    } else if constexpr (XM == XM_WAVE || XM == XM_QUAD) {
+        static_assert(NW == 1 || NW == 2, "XM_WAVE and XM_QUAD hold up to 8 rows");
 #pragma unroll
         for (int j = 0; j < NW; ++j)
             st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j], x_off, 0));
@@ -170,6 +174,42 @@ __device__ __forceinline__ void gemv_x_lds(u32x4 (&xa)[4], const uint8_t *xrow, 
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         xa[b] = *(const u32x4 *)(xrow + 256 * q + 64 * b);
+}
+
+// DPP quad permutation of a 16-byte fragment: lane i of each quad of lanes
+// takes the fragment of lane (CTRL >> 2 i) & 3.
+template <int CTRL>
+__device__ __forceinline__ u32x4 quad_perm(const u32x4 &v)
+{
+    return u32x4{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, CTRL, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, CTRL, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, CTRL, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, CTRL, 0xF, 0xF, false)};
+}
+
+// XM_QUAD: the A operands of a stage.  Live rows sit in row slots c with
+// c mod 4 in {0, 1} (R = 2) or c mod 4 == 0 (R = 1):
+//   R = 1: lane 4i + j loaded block j of the row of slot 4i; lane 4i
+//          gathers blocks 1..3 from lanes 4i + 1 .. 4i + 3;
+//   R = 2: lane 4i + h (h = 0, 1) loaded blocks 0 and 2 of its row, lane
+//          4i + 2 + h blocks 1 and 3 of the same row; the live lanes take
+//          those.
+// Lanes of unused slots end with fragments of other rows: those rows'
+// outputs are never stored.
+template <int R>
+__device__ __forceinline__ void gemv_x_quad(u32x4 (&xa)[4], const GemvStage &st)
+{
+    if constexpr (R == 1) {
+        xa[0] = st.xa[0];
+        xa[1] = quad_perm<0x55>(st.xa[0]);
+        xa[2] = quad_perm<0xAA>(st.xa[0]);
+        xa[3] = quad_perm<0xFF>(st.xa[0]);
+    } else {
+        xa[0] = st.xa[0];
+        xa[1] = quad_perm<0xEE>(st.xa[0]);
+        xa[2] = st.xa[1];
+        xa[3] = quad_perm<0xEE>(st.xa[1]);
+    }
 }
 
 // XM_WAVE: the stage's rows (lane (g, c) of load j holds chunk c of row
@@ -271,9 +311,20 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     // rows that are never stored
     const int xr = slot_row(c);  // the batch row of A row slot c
     in.x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
+    if constexpr (XM == XM_QUAD) {
+        // the quad partner's row and the blocks this lane loads for it
+        const int pc = R == 1 ? (c & ~3) : (c & ~2);
+        const int qr = slot_row(pc);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        in.xw_lane[j] = 4 * j + g < mrows ? (uint32_t)(4 * j + g) * (uint32_t)K * 2u + 16u * c : x_bytes;
+        for (int j = 0; j < 2; ++j) {
+            const int b = R == 1 ? (c & 3) : 2 * j + ((c >> 1) & 1);
+            in.xw_lane[j] = qr < mrows ? (uint32_t)qr * (uint32_t)K * 2u + 64u * (uint32_t)b + 16u * g : x_bytes;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            in.xw_lane[j] = 4 * j + g < mrows ? (uint32_t)(4 * j + g) * (uint32_t)K * 2u + 16u * c : x_bytes;
+    }
     // XM_WAVE: the wave's slot; A rows past the batch read the last row
     // (their outputs are never stored)
     uint8_t *const wslot = xlds + (uint32_t)wave * (4u * R * XW_ROW);
@@ -364,6 +415,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
                 if constexpr (XM == XM_WAVE) {
                     u32x4 xa[4];
                     gemv_x_wave<R>(xa, ring[d], wput, xget);
+                    gemv_quad<BF16, R, SHORT>(ring[d], xa, SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                } else if constexpr (XM == XM_QUAD) {
+                    u32x4 xa[4];
+                    gemv_x_quad<R>(xa, ring[d]);
                     gemv_quad<BF16, R, SHORT>(ring[d], xa, SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
                 } else {
                     gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
@@ -1183,10 +1238,17 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     // 5.7 us); with fewer, longer runs (K = 896, 3584) it is 1-9% slower
     if (sh.split && plan.S / sh.L == 8 && M <= 8)
         sh.xm = XM_WAVE;
+    // measured: from 5 to 8 rows on the other split shapes, x gathered by
+    // DPP (whole 128-byte lines, 16 line requests a stage against the
+    // ring's 32) is 1-2% faster than the ring (k_proj at 5 rows 4.75 ->
+    // 4.67 us, q_proj 5.16 -> 5.07 us); up to 4 rows staging wins
+    if (sh.split && sh.xm == XM_RING && M > 4 && M <= 8)
+        sh.xm = XM_QUAD;
     // Q4_GEMV_XLDS (measurement): 0 = x through the ring, 1 = staged in LDS
-    // (if it fits), 2 = through per-wave LDS slots (up to 8 rows)
-    if (e_xl == 0 || e_xl == 2)
-        sh.xm = e_xl == 2 && M <= 8 ? XM_WAVE : XM_RING;
+    // (if it fits), 2 = through per-wave LDS slots, 3 = gathered by DPP
+    // (both up to 8 rows)
+    if (e_xl == 0 || e_xl == 2 || e_xl == 3)
+        sh.xm = M > 8 || e_xl == 0 ? XM_RING : e_xl == 2 ? XM_WAVE : XM_QUAD;
     if (e_xl == 1)
         sh.xm = fits ? XM_LDS : XM_RING;
     static const int e_tw = env_knob("Q4_GEMV_TW", 0);
@@ -1254,6 +1316,13 @@ static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
         return;
     }
     if constexpr (R <= 2) {
+        if (sh.xm == XM_QUAD) {
+            if (sh.split)
+                launch_gemv_v<BF16, R, 4, true, XM_QUAD>(a);
+            else
+                launch_gemv_v<BF16, R, 4, false, XM_QUAD>(a);
+            return;
+        }
         if (sh.xm == XM_WAVE) {
 #ifdef GEMV_WAVE_DEPTH
             constexpr int DW = GEMV_WAVE_DEPTH;

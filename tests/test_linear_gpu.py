@@ -46,7 +46,8 @@ def test_hand_example_exact(kernel):
 # (M, N, K, bf16): several tiles, ragged N and M tails, K with a short last
 # quad, the smallest K, segment counts 1..16; K above 8192 with a short last
 # quad (the matrix-matrix kernel's 32-row units, split over K); eight runs a
-# tile with a short last quad at 2..8 rows (x through per-wave LDS slots)
+# tile with a short last quad at 2..8 rows (x through per-wave LDS slots);
+# 5..8 rows with fewer runs, one with a short last quad (x gathered by DPP)
 SHAPES = [
     (1, 896, 896, False), (2, 128, 896, False), (4, 4864, 896, False), (3, 896, 4864, False),
     (1, 16, 32, True), (5, 17, 64, True), (16, 40, 96, True), (17, 33, 160, True),
@@ -54,6 +55,7 @@ SHAPES = [
     (100, 130, 640, True), (124, 48, 3584, True), (128, 96, 256, False), (9, 1, 32 * 67, True),
     (40, 50, 8224, True), (70, 150, 9024, False),
     (2, 17, 4128, True), (5, 200, 4128, True), (7, 33, 8224, False), (8, 70, 8224, True),
+    (6, 300, 3616, True), (8, 40, 896, False),
 ]
 
 
