@@ -110,7 +110,7 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
 struct GemvStream {
     __amdgpu_buffer_rsrc_t w, s, x;
     uint32_t w_lane, s_lane, x_lane;  // per-lane byte offsets
-    uint32_t xw_lane[2];              // XM_WAVE: rows g and 4 + g, chunk c
+    uint32_t xw_lane[2];              // XM_WAVE: rows g, 4 + g, chunk c; XM_QUAD: see gemv_x_quad
     uint32_t w_off, s_off;            // scalar offsets of the next refill
 };
 
