@@ -1199,6 +1199,12 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
         L *= 2;
     while (plan.S / L > 8)
         L *= 2;
+    // 257..512 tiles with 2048 < K <= 6144 (where the split form takes over
+    // from the segment form): four runs a tile, so smaller workgroups share
+    // the compute units more evenly (measured: 4608 x 3584 at one row 6.5 ->
+    // 6.0 us, 6144 x 4864 8.2 -> 6.9 us)
+    if (tiles > 256 && tiles <= 512 && plan.G > 16 && plan.G <= 48)
+        L = plan.S / 4;
     sh.L = L;
     sh.tps = (tiles + 2047) / 2048;  // about 2048 streams
     sh.D = 8;
@@ -1435,8 +1441,11 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
         return false;
     const int tiles = (N + 15) / 16;
     // measured on MI355X: with one tile per workgroup or fewer (N <= 4096)
-    // the split form is faster
-    if (tiles <= 256 && e_seg != 2)
+    // the split form is faster; up to 512 tiles also with 3-quad segments
+    // (6144 x 4864 at one row 8.8 -> 6.9 us) and with 2-quad segments up to
+    // 4 rows (4608 x 3584 6.5 -> 6.0 us), not from 5 rows on (6144 x 3584
+    // at 8 rows 7.1 against 7.3 us)
+    if (e_seg != 2 && (tiles <= 256 || (tiles <= 512 && (LQ == 3 || (LQ == 2 && M <= 4)))))
         return false;
     tpw = e_tpw > 0 ? e_tpw : (tiles + 255) / 256;
     const int MR = M < 16 ? M : 16;

@@ -56,6 +56,7 @@ SHAPES = [
     (40, 50, 8224, True), (70, 150, 9024, False),
     (2, 17, 4128, True), (5, 200, 4128, True), (7, 33, 8224, False), (8, 70, 8224, True),
     (6, 300, 3616, True), (8, 40, 896, False),
+    (3, 4100, 3584, True), (2, 4100, 4128, True), (7, 6150, 4864, False),
 ]
 
 
@@ -67,12 +68,13 @@ def test_parity_random(M, N, K, bf16, kernel):
     check(x, bf16, codes, s, kernel)
 
 
-# Wide N (more than 256 column tiles) with 2048 <= K <= 6144 takes the
-# matrix-vector kernel's segment-stationary form: segments of 1, 2 and 3
-# quads, a short last quad, ragged last tile and rows, 1..3 tiles per
-# workgroup with a partial last workgroup.
+# Wide N with 2048 <= K <= 6144 takes the matrix-vector kernel's
+# segment-stationary form (above 256 column tiles with 1-quad segments, above
+# 512 otherwise or from 5 rows on): segments of 1, 2 and 3 quads, a short
+# last quad, ragged last tile and rows, 1..3 tiles per workgroup with a
+# partial last workgroup.
 SEG_SHAPES = [
-    (1, 4100, 2048, True), (2, 4112, 2080, False), (3, 4100, 3584, True), (2, 4100, 4128, True),
+    (1, 4100, 2048, True), (2, 4112, 2080, False), (3, 8210, 3584, True), (2, 8210, 4128, True),
     (9, 4100, 2048, False), (1, 8210, 2048, True), (8, 4352, 3584, True), (16, 4112, 3584, True),
     (13, 8210, 2080, False),
 ]
