@@ -12,13 +12,15 @@
 //    by tile through a ring of D register stages (16-byte contiguous loads,
 //    issued D quads ahead without branches), dequantizes in registers while
 //    reading (the matrix-vector kernel's advantage the page names) and runs
-//    the block dots on MFMA with all (<= 16) rows of x in the A operand.
-//    The runs' subtree roots meet in LDS for the top of the pairwise tree.
+//    the block dots on MFMA with all (<= 16) rows of x in the A operand
+//    (x staged in LDS, passed through per-wave LDS slots, gathered by DPP or
+//    loaded with the ring: see XM_RING).  The runs' subtree roots meet in
+//    LDS for the top of the pairwise tree.
 //
-//  * q4_gemv_seg: the same kernel's form for wide N (more than 256 column
-//    tiles): a workgroup of 16 waves owns a run of column tiles, wave j
-//    owns segment j of all of them and holds that segment of x in
-//    registers, so the workgroup reads x once.
+//  * q4_gemv_seg: the same kernel's form for wide N (more than 256 or 512
+//    column tiles, see seg_shape): a workgroup of 16 waves owns a run of
+//    column tiles, wave j owns segment j of all of them and holds that
+//    segment of x in registers, so the workgroup reads x once.
 //
 //  * q4_gemm_ws: the matrix-matrix kernel for larger M.  A workgroup of
 //    4..8 waves owns an output unit of 16 or 32 rows by one column tile per
