@@ -14,8 +14,8 @@ in HBM before the timed region.
 Printed JSON line: value = achieved algorithmic HBM GB/s over the whole step
 (codes + scales + activations + outputs per call, divided by step time),
 with the dominant kernel's roofline and the fp64 CPU oracle timed on the
-host as a baseline.  The GEMV->GEMM crossover on the layer set and the
-per-M bandwidth are reported under "detail".
+host as a baseline.  The GEMV->GEMM crossover (on the layer set and per
+matrix) and the per-M bandwidth are reported under "detail".
 
 Timing: each step's 48 launches are captured once in a HIP graph (one graph
 per offset into the pool); the timed region replays them between two events on the
@@ -240,8 +240,12 @@ def main() -> int:
     # matrix (the step pool's copies plus clones), so that every launch
     # streams its weights from HBM: the step pool alone holds 14 copies of
     # q_proj (100 MB), which the Infinity Cache would keep.
+    # The per-matrix crossover (M* of each projection alone) is taken on the
+    # same pools, with each kernel forced.
     per_launch = {}
     per_m = per_matrix_m8 = per_launch_us = None
+    xM = list(range(1, 21)) + [24, 28, 32, 48, 64, 96, 128]
+    per_matrix_x = {}
     if not args.no_per_launch:
         pool_bytes = args.pool_gib * (1 << 30)
         for mi, m in enumerate(mats):
@@ -257,6 +261,24 @@ def main() -> int:
                 # clones were freed has been seen up to 5x slower, once
                 per_launch[(mi, M)] = min(time_graphs([g], 1) for _ in range(3)) / len(mpool)  # ms per launch
                 del g
+            if not args.no_crossover:
+                rows = []
+                for M in xM:
+                    t = {}
+                    for kern in ("gemv", "gemm"):
+                        g = capture(lambda M=M, mi=mi, mpool=mpool, kern=kern: [
+                            q4.linear(xs[m.K][:M], w, out=ys[(mi, M)], kernel=kern) for w in mpool])
+                        g.replay()
+                        t[kern] = min(time_graphs([g], 1) for _ in range(2)) / len(mpool) * 1e3  # us
+                        del g
+                    rows.append([M, round(t["gemv"], 2), round(t["gemm"], 2)])
+                mstar_m = None
+                for r in reversed(rows):
+                    if r[2] >= r[1]:
+                        break
+                    mstar_m = r[0]
+                per_matrix_x[m.name] = {"M_star": mstar_m, "rows_M_gemv_us_gemm_us": rows}
+                log("%s: matrix-matrix faster from M* = %s" % (m.name, mstar_m))
             del extra, mpool
             torch.cuda.empty_cache()
         per_m = {}
@@ -394,7 +416,8 @@ def main() -> int:
             mstar = r["M"]
         crossover = {"layer_set_table": table, "M_star": mstar,
                      "T_rule": (mstar - 1) if mstar else None,
-                     "library_T": q4.get_crossover()}
+                     "library_T": q4.get_crossover(),
+                     "per_matrix": per_matrix_x or None}
         log("crossover M* = %s" % mstar)
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step
