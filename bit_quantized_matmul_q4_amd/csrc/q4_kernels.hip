@@ -520,9 +520,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // then outputs [tpw][MR][16] floats.
 // TC: tiles per combine.  Measured on MI355X: with up to 8 tiles per
 // workgroup one combine at the end is fastest (gate at one row 10.7 ->
-// 10.4 us); with more tiles (gate|up, the LM head) combining every 2 tiles
-// is, and above 8 rows 1 (the partials take 4 KB a row).
-__host__ __device__ inline int seg_tc(int M, int tpw) { return M > 8 ? 1 : tpw <= 8 ? 8 : 2; }
+// 10.4 us, at 9 rows 13.2 -> 12.4 us); with more tiles (gate|up, the LM
+// head) combining every 2 tiles is, and above 8 rows every tile (the
+// partials take 4 KB a row).
+__host__ __device__ inline int seg_tc(int M, int tpw) { return tpw <= 8 ? 8 : M > 8 ? 1 : 2; }
 __host__ __device__ inline int seg_nbuf(int tc, int tpw) { return tpw <= tc ? 1 : 2; }
 // Ring depth of the segment form (a multiple of LQ).  Measured on MI355X:
 // 4 stages beat 6, 8 and 10 (a deep per-wave prefetch delays the data each
@@ -1397,6 +1398,8 @@ template <bool BF16, int R, int LQ>
 static void launch_seg_v(const GemvArgs &a)
 {
     if constexpr (R == 4) {
+        if (seg_tc(a.M, a.tps) == 8)
+            return launch_seg_t<BF16, R, LQ, 8>(a);
         if (seg_tc(a.M, a.tps) == 1)
             return launch_seg_t<BF16, R, LQ, 1>(a);
     } else {
