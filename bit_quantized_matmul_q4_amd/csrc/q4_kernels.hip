@@ -1235,24 +1235,17 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     const size_t xbytes = rows * gemv_xrow_bytes(K) + 256;
     const size_t roots = sh.split ? 0 : (size_t)4 * sh.tps * 256 * sizeof(float);
     const bool fits = roots + xbytes <= GEMV_XLDS_MAX;
-    // measured on MI355X, weights streaming from HBM: staged x pays for up
-    // to 4 rows (896 x 4864 6.6 -> 5.0 us, 4096 x 4096 6.1 -> 5.4 us,
-    // k_proj 4.5 -> 4.3 us, within 2% elsewhere); from 5 rows on its LDS
-    // footprint caps the waves a compute unit can hold (q_proj at 8 rows
-    // 5.4 -> 5.6 us)
+    // Measured on MI355X, weights streaming from HBM.  Split form up to 8
+    // rows: with eight runs a tile (K = 4096, 4864, 8192, 18944) x through
+    // per-wave slots (down_proj at 4 / 8 rows 11.9 / 15.8 -> 10.6 / 13.3 us
+    // against the staged / ring forms), otherwise x gathered by DPP (at 1-4
+    // rows against staging: 4864 x 896 4.3 -> 3.8 us, 2048 x 2048 3.9 ->
+    // 3.6 us, 4608 x 3584 6.1 -> 5.8 us; at 5-8 rows against the ring:
+    // k_proj 4.75 -> 4.67 us).  One stream per wave (very wide N): x staged
+    // up to 4 rows, else in the ring.
     sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
-    // measured on MI355X: with eight runs a tile (K = 4096, 4864, 8192,
-    // 18944) x through per-wave slots beats both up to 8 rows (down_proj at
-    // 4 / 8 rows 11.9 / 15.8 -> 10.6 / 13.3 us, 4096 x 4096 5.4 / 6.4 -> 5.0 /
-    // 5.7 us); with fewer, longer runs (K = 896, 3584) it is 1-9% slower
-    if (sh.split && plan.S / sh.L == 8 && M <= 8)
-        sh.xm = XM_WAVE;
-    // measured: from 5 to 8 rows on the other split shapes, x gathered by
-    // DPP (whole 128-byte lines, 16 line requests a stage against the
-    // ring's 32) is 1-2% faster than the ring (k_proj at 5 rows 4.75 ->
-    // 4.67 us, q_proj 5.16 -> 5.07 us); up to 4 rows staging wins
-    if (sh.split && sh.xm == XM_RING && M > 4 && M <= 8)
-        sh.xm = XM_QUAD;
+    if (sh.split && M <= 8)
+        sh.xm = plan.S / sh.L == 8 ? XM_WAVE : XM_QUAD;
     // Q4_GEMV_XLDS (measurement): 0 = x through the ring, 1 = staged in LDS
     // (if it fits), 2 = through per-wave LDS slots, 3 = gathered by DPP
     // (both up to 8 rows)

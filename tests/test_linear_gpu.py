@@ -47,7 +47,9 @@ def test_hand_example_exact(kernel):
 # quad, the smallest K, segment counts 1..16; K above 8192 with a short last
 # quad (the matrix-matrix kernel's 32-row units, split over K); eight runs a
 # tile with a short last quad at 2..8 rows (x through per-wave LDS slots);
-# 5..8 rows with fewer runs, one with a short last quad (x gathered by DPP)
+# 5..8 rows with fewer runs, one with a short last quad (x gathered by DPP);
+# 4097 column tiles with K outside the segment form's range (one stream per
+# wave: x staged in LDS up to 4 rows, else in the ring)
 SHAPES = [
     (1, 896, 896, False), (2, 128, 896, False), (4, 4864, 896, False), (3, 896, 4864, False),
     (1, 16, 32, True), (5, 17, 64, True), (16, 40, 96, True), (17, 33, 160, True),
@@ -57,6 +59,7 @@ SHAPES = [
     (2, 17, 4128, True), (5, 200, 4128, True), (7, 33, 8224, False), (8, 70, 8224, True),
     (6, 300, 3616, True), (8, 40, 896, False),
     (3, 4100, 3584, True), (2, 4100, 4128, True), (7, 6150, 4864, False),
+    (3, 65552, 1024, True), (6, 65552, 1024, False),
 ]
 
 
