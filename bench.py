@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-stream", action="store_true", help="skip the 28-layer decode weight stream")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-launch step")
     ap.add_argument("--no-schemes", action="store_true", help="skip the pages' switching schemes comparison")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the 0.5B-shaped layer set and the single 896 x 896 matvec")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-per-launch", action="store_true",
                     help="skip the per-matrix launch timings (per-M and per-matrix GB/s)")
@@ -350,6 +352,46 @@ def main() -> int:
         del layers, head
         torch.cuda.empty_cache()
 
+    # ---- the small workloads: the single 896 x 896 matvec at M = 1 and the
+    # Qwen2.5-0.5B-shaped layer set at M = 1, 2, 4, fp16 activations; each
+    # call on its own weight copy from a pool of about half the step pool's
+    # size, so the weights stream from HBM
+    small = None
+    if not args.no_small:
+        small = {}
+        for wl in (1, 2):
+            spec = synth.WORKLOADS[wl]
+            smats = spec["matrices"]
+            sbytes = sum(sum(q4.packed_sizes(m.N, m.K)) for m in smats)
+            SP = max(2, int(np.ceil(args.pool_gib * (1 << 30) / 2 / sbytes)))
+            sbase = []
+            for mi, m in enumerate(smats):
+                wq_t, sc_t = synth.packed_weight(m.N, m.K, wl, mi)
+                sbase.append(q4.Q4Weight(torch.from_numpy(wq_t).to(dev),
+                                         torch.from_numpy(sc_t.view(np.int16)).to(dev).view(torch.float16), m.N, m.K))
+            spool = [[q4.Q4Weight(w.codes.clone(), w.scales.clone(), w.N, w.K) for w in sbase] for _ in range(SP)]
+            Mx = max(spec["Ms"])
+            sx = {}
+            for K in sorted({m.K for m in smats}):
+                xb = synth.activations(Mx, K, spec["x"], wl, 100 + K)
+                sx[K] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.float16)
+            rec = {}
+            for M in spec["Ms"]:
+                ysm = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in smats]
+                g = capture(lambda M=M, ysm=ysm: [q4.linear(sx[m.K][:M], spool[p][mi], out=ysm[mi])
+                                                  for p in range(SP) for mi, m in enumerate(smats)])
+                g.replay()
+                ms = min(time_graphs([g], 1) for _ in range(3)) / SP  # per pass over the set
+                del g
+                nb = sum(synth.algorithmic_bytes(M, m.N, m.K) for m in smats)
+                rec[str(M)] = {"us": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                               "rows_per_s": round(M / (ms * 1e-3), 1)}
+            small[spec["name"]] = {"matrices": ["%s %dx%d" % (m.name, m.N, m.K) for m in smats],
+                                   "x": spec["x"], "weight_copies": SP, "per_M": rec}
+            log("%s: %s" % (spec["name"], rec))
+            del spool, sbase, sx
+            torch.cuda.empty_cache()
+
     # ---- the pages' kernel-switching schemes as comparators, on the layer
     # set at the pages' row counts: 1..5 (one row per request) and the
     # continuous-batching iterations 8, 19, 44, 85 tokens and the 124-row
@@ -477,7 +519,7 @@ def main() -> int:
                      "avg_launch_us": round(launch_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "detail": {"per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "per_launch_us": per_launch_us, "fused_step": fused_step,
-                   "decode_stream_7b": stream, "switching_schemes": schemes, "crossover": crossover},
+                   "decode_stream_7b": stream, "small_workloads": small, "switching_schemes": schemes, "crossover": crossover},
     }
     line = json.dumps(out)
     if args.detail_json:
