@@ -723,7 +723,11 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 #ifdef GW_DW_FIXED
 constexpr int GW_DW = GW_DW_FIXED;
 #else
-constexpr int GW_DW = 6;  // weight ring stages (registers; 6 beat 4 and 8 on gate)
+// weight ring stages (registers).  Measured on MI355X with the x register
+// sets below: 4 stages beat 6 at 17-32 rows (q_proj at 17 rows 9.9 -> 9.3
+// us, gate 24.4 -> 23.6 us) and match them at 124 (fewer registers: 130
+// instead of 148)
+constexpr int GW_DW = 4;
 #endif
 
 // The activation stage holds, per row tile, 16 rows of the quad's 256 bytes
@@ -850,7 +854,7 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     // no memory access).
     const int xr = lane >> 4, xj = lane & 15;  // row in the chunk, LDS granule
     // x register sets: x is loaded XSETS - 1 quads ahead of its use
-    constexpr int XSETS = RT == 1 ? 6 : 3;  // six at two row tiles cost occupancy (measured slower)
+    constexpr int XSETS = RT == 1 ? 4 : 2;  // a divisor of GW_DW; more at two row tiles cost occupancy
     u32x4 xreg[XSETS][RT];
     auto load_x = [&](u32x4 (&xv)[RT], int qq) {
         const bool live = qq < nquads;
