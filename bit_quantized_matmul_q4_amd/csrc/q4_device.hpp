@@ -9,18 +9,22 @@
 // kernels summed in different orders and dequantized at different times, so
 // a batching decision changed the numbers written to the KV cache.
 //
-// The order (version 2), for output (m, n), K = 32 * nb:
+// The order (version 3), for output (m, n), K = 32 * nb:
 //   quads:    G = ceil(nb / 4) groups of 4 blocks; the last may be short.
 //   segments: S = min(16, 2^floor(log2 G)); segment j covers quads
 //             [floor(j G / S), floor((j+1) G / S)), i.e. blocks
 //             [4 floor(j G / S), min(nb, 4 floor((j+1) G / S))).
-//   block dot: s_b = fl(D - E) for element (m, n) of two
-//             v_mfma_f32_16x16x32_{bf16,f16} with C = 0 and A row =
-//             x[m][32b .. 32b+31] in natural k order: D with B column =
-//             V + q[n][32b+k], E with every B entry = V + 8, where V = 128
-//             (bf16) or 1024 (fp16).  Both B operands are exact in x's type,
-//             so s_b approximates sum_k x (q - 8); a block of all-8 codes
-//             gives D = E and s_b = 0 exactly.  E depends on x only.
+//   block dot s_b, one v_mfma_f32_16x16x32_{bf16,f16} (C = 0) per product
+//             with A row = x[m][32b .. 32b+31] in natural k order:
+//             fp16 x: s_b = D, B column = q[n][32b+k] - 8 (exact in fp16),
+//               so every product is exact and a zero weight adds exactly 0;
+//             bf16 x: s_b = fl(D - E), D with B column = 16 + q[n][32b+k],
+//               E with every B entry = 24 (both exact in bf16; E depends on
+//               x only); a block of all-8 codes gives D = E and s_b = 0
+//               exactly.  (bf16 has no packed add on this target, so an
+//               exact q - 8 operand would cost about three times the
+//               dequantization work; the offset 16 keeps the cancellation
+//               to a factor 24 of the weight step.)
 //   segment:  p_j = +0; for b ascending: p_j = fmaf(d[n][b], s_b, p_j).
 //   tree:     for h = 1, 2, 4, .. S/2: p_j = p_j + p_{j+h} for j % 2h == 0.
 //   output:   y[m][n] = p_0.
@@ -33,8 +37,8 @@
 // 4 i + 3 of lane l holds the codes of column n, k = 32 b + 8 g + r,
 // r = 0..7, with code r at bit 4 (r / 2) + 16 (r % 2).  So one 16-byte load
 // gives lane (g, c) its B-operand codes of the tile's four block dots, and
-// a mask-and-or per pair of k turns them into operand words.  Then 64 fp16
-// scales, [c][i].  Padding (n >= N, b >= nb) is zero.
+// a shift and a mask-and-or per pair of k turn them into operand words.
+// Then 64 fp16 scales, [c][i].  Padding (n >= N, b >= nb) is zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,57 +56,77 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- dequant
-// The 16-bit pattern (V_BITS | q), q in 0..15, is V + q exactly: V = 128 in
-// bf16 (0x4300; the ulp on [128, 256) is 1) and V = 1024 in fp16 (0x6400).
+// bf16: the 16-bit pattern 0x4180 | (q << 3), q in 0..15, is 16 + q exactly
+// (16 = 0x4180, the code in the top four of the seven mantissa bits).
+// fp16: 0x6400 | q is 1024 + q exactly (the ulp on [1024, 2048) is 1), and
+// one packed fp16 add of -1032 (exact: the result is an integer in -8..7)
+// leaves q - 8.
 template <bool BF16>
-constexpr uint32_t kMagic = BF16 ? 0x43004300u : 0x64006400u;
-// B operand of the correction dot E: V + 8 in every entry.
+constexpr uint32_t kMask = BF16 ? 0x00780078u : 0x000F000Fu;
 template <bool BF16>
-constexpr uint32_t kOffset = BF16 ? 0x43084308u : 0x64086408u;
+constexpr uint32_t kMagic = BF16 ? 0x41804180u : 0x64006400u;
+constexpr uint32_t kF16Bias = 0xE408E408u;  // -1032, -1032 (binary16)
+// B operand of the bf16 correction dot E: 24 in every entry.
+constexpr uint32_t kBf16Offset = 0x41C041C0u;
+// Whether the block dot carries the correction E (bf16) or is exact (fp16).
+template <bool BF16>
+constexpr bool kCorrected = BF16;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One packed word (code r at bit 4 (r / 2) + 16 (r % 2)) -> the eight
-// operand values V + q in natural k order, two per dword: one mask-and-or
-// per dword.  mask = 0x000F000F and magic = kMagic must arrive as opaque
-// registers (see Dequant): as literals the compiler splits each step in two
-// (this target's three-operand instructions take no literal).
+// operand values in natural k order, two per dword.  bf16: the pair's codes
+// moved to bits 3..6 of each half (pair 0 up by 3, pairs 1..3 down by 1, 5,
+// 9), masked and or-ed with the magic.  fp16: masked in place and or-ed,
+// then the packed add.  mask, magic and bias must arrive as opaque registers
+// (see Dequant): as literals the compiler splits each step in two (this
+// target's three-operand instructions take no literal).
 template <bool BF16>
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, uint32_t mask, uint32_t magic)
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, uint32_t mask, uint32_t magic, uint32_t bias)
 {
     u32x4 r;
-    r.x = (w & mask) | magic;
-    r.y = ((w >> 4) & mask) | magic;
-    r.z = ((w >> 8) & mask) | magic;
-    r.w = ((w >> 12) & mask) | magic;
+    if constexpr (BF16) {
+        r.x = ((w << 3) & mask) | magic;
+        r.y = ((w >> 1) & mask) | magic;
+        r.z = ((w >> 5) & mask) | magic;
+        r.w = ((w >> 9) & mask) | magic;
+    } else {
+        const f16x2 b = __builtin_bit_cast(f16x2, bias);
+        r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w & mask) | magic) + b);
+        r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 4) & mask) | magic) + b);
+        r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 8) & mask) | magic) + b);
+        r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 12) & mask) | magic) + b);
+    }
     return r;
 }
 
-// The dequant constants in registers the compiler cannot fold: the mask in a
-// scalar register, the magic in a vector one (one scalar operand per
-// instruction on this target).  The empty statements emit no instructions.
-// The correction's B operand (V + 8 everywhere) is built once the same way,
-// so the compiler keeps it in four registers instead of rebuilding it for
-// every block dot.
+// The dequant constants in registers the compiler cannot fold: the mask and
+// the fp16 bias in scalar registers, the magic in a vector one (one scalar
+// operand per instruction on this target).  The empty statements emit no
+// instructions.  The bf16 correction's B operand (24 everywhere) is built
+// once the same way, so the compiler keeps it in four registers instead of
+// rebuilding it for every block dot.
 template <bool BF16>
 struct Dequant {
-    uint32_t mask, magic;
+    uint32_t mask, magic, bias;
     u32x4 offset;
     __device__ __forceinline__ Dequant()
     {
-        mask = 0x000F000Fu;
+        mask = kMask<BF16>;
         magic = kMagic<BF16>;
-        offset = (u32x4){kOffset<BF16>, kOffset<BF16>, kOffset<BF16>, kOffset<BF16>};
+        bias = kF16Bias;
         asm volatile("" : "+s"(mask));
         asm volatile("" : "+v"(magic));
-        asm volatile("" : "+v"(offset));
+        if constexpr (BF16) {
+            offset = (u32x4){kBf16Offset, kBf16Offset, kBf16Offset, kBf16Offset};
+            asm volatile("" : "+v"(offset));
+        } else {
+            offset = (u32x4){0u, 0u, 0u, 0u};
+            asm volatile("" : "+s"(bias));
+        }
     }
-    __device__ __forceinline__ u32x4 operator()(uint32_t w) const { return dequant8<BF16>(w, mask, magic); }
+    __device__ __forceinline__ u32x4 operator()(uint32_t w) const { return dequant8<BF16>(w, mask, magic, bias); }
 };
-
-template <bool BF16>
-__device__ __forceinline__ u32x4 offset_operand()
-{
-    return (u32x4){kOffset<BF16>, kOffset<BF16>, kOffset<BF16>, kOffset<BF16>};
-}
 
 // ---------------------------------------------------------------- BlockDot
 // One v_mfma_f32_16x16x32 with C = 0.  Lane l supplies A[l % 16][8 (l/16) ..
@@ -125,14 +149,26 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// p = fmaf(d, D - E, p) for the four accumulator rows a lane holds (the
-// difference rounds first: -ffp-contract=off keeps it a separate step).
+// The block dot's value from the matrix-core results: fl(D - E) (bf16; the
+// difference rounds first: -ffp-contract=off keeps it a separate step) or
+// D itself (fp16, exact operands).
+template <bool BF16>
+__device__ __forceinline__ float block_value(float D, float E)
+{
+    if constexpr (kCorrected<BF16>)
+        return D - E;
+    else
+        return D;
+}
+
+// p = fmaf(d, s_b, p) for the four accumulator rows a lane holds.
+template <bool BF16>
 __device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 D, f32x4 E)
 {
-    p.x = __builtin_fmaf(d, D.x - E.x, p.x);
-    p.y = __builtin_fmaf(d, D.y - E.y, p.y);
-    p.z = __builtin_fmaf(d, D.z - E.z, p.z);
-    p.w = __builtin_fmaf(d, D.w - E.w, p.w);
+    p.x = __builtin_fmaf(d, block_value<BF16>(D.x, E.x), p.x);
+    p.y = __builtin_fmaf(d, block_value<BF16>(D.y, E.y), p.y);
+    p.z = __builtin_fmaf(d, block_value<BF16>(D.z, E.z), p.z);
+    p.w = __builtin_fmaf(d, block_value<BF16>(D.w, E.w), p.w);
 }
 
 // Streaming form of the pairwise tree for one wave that owns an aligned run

@@ -35,7 +35,6 @@
 //  * q4_quantize_kernel: dense weights -> canonical codes and scales.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <algorithm>
 
@@ -45,10 +44,14 @@
 namespace q4 {
 
 // =================================================================== GEMV
-// Buffer resource over a wave-uniform base.  Every offset below is kept in
-// range by construction (clamped stream indices); the resource form lets the
-// per-load offsets live in scalar registers, so streaming costs no vector
-// address arithmetic.
+// Buffer resource over a wave-uniform base, with the exact byte range of the
+// data a wave may read.  Every load below passes its whole offset (the
+// lane's part plus the running stream position) as the vector offset, which
+// the raw-buffer range check covers: a load whose vector offset is at or
+// past the range returns zeros and makes no memory access.  The kernels use
+// that on purpose for refills past a stream's end and for row slots past the
+// batch, and pass a scalar offset of zero everywhere, so no read can leave
+// its buffer whether or not the check also counts the scalar offset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes = 0xFFFFFFFFu)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -89,7 +92,10 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         D[i] = blockdot<BF16>(xa[i], dq(w[i]));
-        E[i] = blockdot<BF16>(xa[i], dq.offset);
+        if constexpr (kCorrected<BF16>)
+            E[i] = blockdot<BF16>(xa[i], dq.offset);
+        else
+            E[i] = D[i];  // unused
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -97,7 +103,7 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
             const float d = half_bits_to_float(h[i]);
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                p[r] = __builtin_fmaf(d, D[i][r] - E[i][r], p[r]);
+                p[r] = __builtin_fmaf(d, block_value<BF16>(D[i][r], E[i][r]), p[r]);
         }
     }
 }
@@ -105,10 +111,10 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
 // The wave's stream is a contiguous run of tile-quads: quad i of the stream
 // sits at code byte 1024 i and scale byte 128 i from the wave's base, and is
 // quad q0 + (i mod RQ) of K.  The code and scale resources span exactly the
-// stream, and the range check covers the scalar offset: the ring's refills
-// past the end return zero without a memory access, with no clamp or test.
-// x blocks past nb (a short last quad) read whatever follows (the next row,
-// or zero past the slice); their block dots are skipped.
+// stream, so the ring's refills past the end (vector offsets at or past the
+// range) return zero without a memory access, with no clamp or test.  x
+// blocks past nb (a short last quad) read whatever follows (the next row, or
+// zero past the slice); their block dots are skipped.
 struct GemvStream {
     __amdgpu_buffer_rsrc_t w, s, x;
     uint32_t w_lane, s_lane, x_lane;  // per-lane byte offsets
@@ -152,18 +158,20 @@ __device__ __forceinline__ void issue_fence()
 template <int XM, int NW>
 __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
-    st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane, in.w_off, kWeightLoadPolicy));
-    st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane, in.s_off, kWeightLoadPolicy));
+    st.w = __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane + in.w_off, 0, kWeightLoadPolicy));
+    st.s = __builtin_bit_cast(u32x2,
+                              __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane + in.s_off, 0, kWeightLoadPolicy));
     if constexpr (XM == XM_RING) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b, x_off, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b + x_off, 0, 0));
     } else if constexpr (XM == XM_WAVE || XM == XM_QUAD) {
         static_assert(NW == 1 || NW == 2, "XM_WAVE and XM_QUAD hold up to 8 rows");
 #pragma unroll
         for (int j = 0; j < NW; ++j)
-            st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j], x_off, 0));
+            st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j] + x_off, 0, 0));
     }
     in.w_off += 1024;
     in.s_off += 128;
@@ -532,11 +540,7 @@ __host__ __device__ inline int seg_nbuf(int tc, int tpw) { return tpw <= tc ? 1 
 template <int R, int LQ>
 constexpr int seg_depth()
 {
-#ifdef SEG_DEPTH_FIXED
-    return SEG_DEPTH_FIXED % LQ == 0 ? SEG_DEPTH_FIXED : 6;
-#else
     return LQ == 3 ? 6 : 4;
-#endif
 }
 
 __device__ __forceinline__ void workgroup_barrier_lds()
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             xs[q][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rx, x_lane + 64u * b, 256u * (qs + min(q, len - 1)), 0));
+                                                     rx, x_lane + 64u * b + 256u * (qs + min(q, len - 1)), 0, 0));
 
     // the stream: tiles t_first .. t_first + ntiles - 1, quads qs .. qs + LQ - 1
     const uint32_t tile_b = (uint32_t)G * 1024u, tile_s = (uint32_t)G * 128u;
@@ -603,8 +607,8 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         const bool live = q < len && pos < npos;
         const uint32_t wo = live ? (uint32_t)i * tile_b + 1024u * (qs + q) : w_range;
         const uint32_t so = live ? (uint32_t)i * tile_s + 128u * (qs + q) : s_range;
-        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane, wo, kWeightLoadPolicy));
-        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane, so, kWeightLoadPolicy));
+        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + wo, 0, kWeightLoadPolicy));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane + so, 0, kWeightLoadPolicy));
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -713,22 +717,18 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 // swizzled; see gemm_ws_a_offset), are loaded by the waves in chunks of four
 // rows into registers two quads ahead and written to a two-stage LDS ring
 // one quad ahead; one barrier per quad publishes a stage.  Per block a wave
-// dequantizes its B operand once for its RT row tiles and runs 2 RT block
-// dots (D and the correction E of each row tile).
+// dequantizes its B operand once for its RT row tiles and runs RT block
+// dots (bf16: 2 RT, D and the correction E of each row tile).
 //
 // The grid is one-dimensional over (column unit, row unit) and K-groups in y:
 // workgroup id -> column unit 8 (id / 8 nru) + id % 8, row unit (id / 8) %
 // nru, so the row units of one column unit (which read the same weights) are
 // eight ids apart: dispatched together, on the same XCD and its L2.
-#ifdef GW_DW_FIXED
-constexpr int GW_DW = GW_DW_FIXED;
-#else
 // weight ring stages (registers).  Measured on MI355X with the x register
 // sets below: 4 stages beat 6 at 17-32 rows (q_proj at 17 rows 9.9 -> 9.3
 // us, gate 24.4 -> 23.6 us) and match them at 124 (fewer registers: 130
 // instead of 148)
 constexpr int GW_DW = 4;
-#endif
 
 // The activation stage holds, per row tile, 16 rows of the quad's 256 bytes
 // (4 KB); row c's 16-byte granule j sits at granule j ^ c.  One load
@@ -771,14 +771,18 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
             B[i] = dq(wd[i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            E[i] = blockdot<BF16>(A[i], dq.offset);
+            if constexpr (kCorrected<BF16>)
+                E[i] = blockdot<BF16>(A[i], dq.offset);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
             Dm[i] = blockdot<BF16>(A[i], B[i]);
+            if constexpr (!kCorrected<BF16>)
+                E[i] = Dm[i];  // unused
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (!SHORT || i < nq)  // blocks past a short last quad: not accumulated
-                scale_accumulate(p[0], scale(i), Dm[i], E[i]);
+                scale_accumulate<BF16>(p[0], scale(i), Dm[i], E[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -792,14 +796,18 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
                 f32x4 E[RT], Dm[RT];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    E[rt] = blockdot<BF16>(A[rt], dq.offset);
+                    if constexpr (kCorrected<BF16>)
+                        E[rt] = blockdot<BF16>(A[rt], dq.offset);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
+                for (int rt = 0; rt < RT; ++rt) {
                     Dm[rt] = blockdot<BF16>(A[rt], B);
+                    if constexpr (!kCorrected<BF16>)
+                        E[rt] = Dm[rt];  // unused
+                }
                 const float dsc = scale(i);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    scale_accumulate(p[rt], dsc, Dm[rt], E[rt]);
+                    scale_accumulate<BF16>(p[rt], dsc, Dm[rt], E[rt]);
             }
         }
     }
@@ -886,8 +894,9 @@ __global__ __launch_bounds__(512) void q4_gemm_ws(const uint16_t *__restrict__ x
     WStage ring[GW_DW];
     uint32_t w_off = 0, s_off = 0;
     auto issue_w = [&](WStage &st) {
-        st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane, w_off, kWeightLoadPolicy));
-        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 8u * c, s_off, kWeightLoadPolicy));
+        st.w = __builtin_bit_cast(u32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rw, 16u * lane + w_off, 0, kWeightLoadPolicy));
+        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, 8u * c + s_off, 0, kWeightLoadPolicy));
         w_off += 1024u;
         s_off += 128u;
     };
@@ -1167,14 +1176,8 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict_
 // ============================================================== launchers
 // Launch shape of the GEMV; none of it changes the bits.  Wide N: one
 // stream per wave over all of K, `tps` tiles per stream.  Narrow N: one
-// workgroup per column tile, W = S / L waves over runs of L segments.
-// Q4_GEMV_SPLIT (0/1), Q4_GEMV_RUN (L), Q4_GEMV_TPS and Q4_GEMV_DEPTH (4/8)
-// override the heuristic (tuning only).
-static int env_knob(const char *name, int dflt)
-{
-    const char *v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
+// workgroup per column tile, W = S / L waves over runs of L segments.  The
+// shape depends on (M, N, K) only.
 
 struct GemvShape {
     bool split;
@@ -1215,20 +1218,7 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     sh.L = L;
     sh.tps = (tiles + 2047) / 2048;  // about 2048 streams
     sh.D = 8;
-    static const int e_split = env_knob("Q4_GEMV_SPLIT", -1);
-    static const int e_run = env_knob("Q4_GEMV_RUN", 0);
-    static const int e_tps = env_knob("Q4_GEMV_TPS", 0);
-    static const int e_d = env_knob("Q4_GEMV_DEPTH", 0);
-    static const int e_xl = env_knob("Q4_GEMV_XLDS", -1);
-    if (e_split == 0 || e_split == 1)
-        sh.split = e_split == 1;
-    if (e_run > 0 && (e_run & (e_run - 1)) == 0 && e_run <= plan.S && plan.S / e_run <= 8)
-        sh.L = e_run;
-    if (e_tps > 0)
-        sh.tps = e_tps;
     sh.tps = sh.tps < GEMV_TPS_MAX ? sh.tps : GEMV_TPS_MAX;
-    if (e_d == 4 || e_d == 8)
-        sh.D = e_d;
     if (!sh.split)
         sh.L = plan.S;  // one run of all S segments
     // a stream's byte offsets stay below 2^31
@@ -1250,17 +1240,7 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
     if (sh.split && M <= 8)
         sh.xm = plan.S / sh.L == 8 ? XM_WAVE : XM_QUAD;
-    // Q4_GEMV_XLDS (measurement): 0 = x through the ring, 1 = staged in LDS
-    // (if it fits), 2 = through per-wave LDS slots, 3 = gathered by DPP
-    // (both up to 8 rows)
-    if (e_xl == 0 || e_xl == 2 || e_xl == 3)
-        sh.xm = M > 8 || e_xl == 0 ? XM_RING : e_xl == 2 ? XM_WAVE : XM_QUAD;
-    if (e_xl == 1)
-        sh.xm = fits ? XM_LDS : XM_RING;
-    static const int e_tw = env_knob("Q4_GEMV_TW", 0);
     sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
-    if (e_tw == 1 || e_tw == 2 || e_tw == 4)
-        sh.tw = sh.split && sh.xm == XM_LDS && e_tw * (plan.S / sh.L) <= 8 ? e_tw : 1;
     if (sh.xm != XM_LDS && sh.split)
         sh.D = 4;  // x rides in the ring: up to 22 registers a stage
     const int waves = sh.split ? (plan.S / sh.L) * sh.tw : 4;
@@ -1310,11 +1290,7 @@ template <bool BF16, int R>
 static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
 {
     if (sh.xm == XM_LDS) {
-#ifdef GEMV_XL_DEPTH
-        constexpr int DX = GEMV_XL_DEPTH;
-#else
         constexpr int DX = 4;  // measured: 4 beats 6 and 8 (down_proj, M <= 4)
-#endif
         if (sh.split)
             launch_gemv_v<BF16, R, DX, true, XM_LDS>(a);
         else
@@ -1330,11 +1306,7 @@ static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
             return;
         }
         if (sh.xm == XM_WAVE) {
-#ifdef GEMV_WAVE_DEPTH
-            constexpr int DW = GEMV_WAVE_DEPTH;
-#else
             constexpr int DW = 4;
-#endif
             if (sh.split)
                 launch_gemv_v<BF16, R, DW, true, XM_WAVE>(a);
             else
@@ -1343,11 +1315,7 @@ static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
         }
     }
     if (sh.split) {
-#ifdef GEMV_SPLIT_DEPTH
-        launch_gemv_v<BF16, R, GEMV_SPLIT_DEPTH, true, XM_RING>(a);
-#else
         launch_gemv_v<BF16, R, 4, true, XM_RING>(a);
-#endif
     } else if (sh.D == 4) {
         launch_gemv_v<BF16, R, 4, false, XM_RING>(a);
     } else {
@@ -1411,6 +1379,8 @@ static void launch_seg_r(int LQ, const GemvArgs &a)
 {
     if (LQ == 1)
         launch_seg_v<BF16, R, 1>(a);
+    else if constexpr (R == 4)  // seg_shape: no 3-quad segments at R = 4
+        launch_seg_v<BF16, R, 2>(a);
     else if (LQ == 2)
         launch_seg_v<BF16, R, 2>(a);
     else
@@ -1430,13 +1400,10 @@ static void launch_seg_b(int R, int LQ, const GemvArgs &a)
 
 // The segment-stationary form applies with S = 16 segments of at most 3
 // quads, more than 256 column tiles and its LDS within 160 KB.  tpw: tiles
-// per workgroup, about one workgroup per compute unit.  Q4_GEMV_SEG=0 turns
-// it off, =2 lifts the tile-count rule (both for measurement).
+// per workgroup, about one workgroup per compute unit.
 static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
 {
-    static const int e_seg = env_knob("Q4_GEMV_SEG", 1);
-    static const int e_tpw = env_knob("Q4_GEMV_SEG_TPW", 0);
-    if (!e_seg || plan.S != 16)
+    if (plan.S != 16)
         return false;
     LQ = (plan.G + 15) / 16;
     if (LQ > 3 || (LQ == 3 && M > 8))  // 3-quad segments at R = 4: 128 registers do not hold them
@@ -1447,9 +1414,9 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
     // (6144 x 4864 at one row 8.8 -> 6.9 us) and with 2-quad segments up to
     // 4 rows (4608 x 3584 6.5 -> 6.0 us), not from 5 rows on (6144 x 3584
     // at 8 rows 7.1 against 7.3 us)
-    if (e_seg != 2 && (tiles <= 256 || (tiles <= 512 && (LQ == 3 || (LQ == 2 && M <= 4)))))
+    if (tiles <= 256 || (tiles <= 512 && (LQ == 3 || (LQ == 2 && M <= 4))))
         return false;
-    tpw = e_tpw > 0 ? e_tpw : (tiles + 255) / 256;
+    tpw = (tiles + 255) / 256;
     const int MR = M < 16 ? M : 16;
     const int tc = seg_tc(M, tpw);
     lds = (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw);
@@ -1541,11 +1508,8 @@ static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
 {
     const Plan plan = make_plan(K);
     GemmWsShape sh;
-    static const int e_rt = env_knob("Q4_GEMM_RT", 0);  // for measurement
     const int tiles = (N + 15) / 16;
     int rt = K > 8192 || (M > 64 && tiles >= 1024) ? 2 : 1;
-    if (e_rt == 1 || e_rt == 2)
-        rt = e_rt;
     // 16 RT rows of x stay below 2^31 bytes (32-bit offsets)
     if ((long long)32 * rt * K >= (1LL << 31))
         rt = 1;  // (K <= 2^25 keeps 16 rows below 2^31 bytes)
@@ -1554,17 +1518,12 @@ static GemmWsShape gemm_ws_shape(int M, int N, int K, size_t workspace_bytes)
     sh.RT = (rows + 15) / 16;
     // four waves (column tiles) per workgroup: measured faster than eight at
     // M = 17..32 (the barrier holds fewer waves in step) and no slower above
-    static const int e_ct = env_knob("Q4_GEMM_CT", 0);
-    sh.CT = e_ct >= 4 && e_ct <= 8 ? e_ct : 4;
+    sh.CT = 4;
     sh.ncu = (tiles + sh.CT - 1) / sh.CT;
     sh.gk = 1;
     while (sh.gk < plan.S && (long long)sh.ncu * sh.nru * sh.gk < kComputeUnits &&
            (size_t)(2 * sh.gk) * M * N * sizeof(float) <= workspace_bytes)
         sh.gk *= 2;
-    static const int e_gk = env_knob("Q4_GEMM_GK", 0);  // for measurement: forced split (power of two)
-    if (e_gk > 0 && (e_gk & (e_gk - 1)) == 0 && e_gk <= plan.S &&
-        (e_gk == 1 || (size_t)e_gk * M * N * sizeof(float) <= workspace_bytes))
-        sh.gk = e_gk;
     return sh;
 }
 

@@ -31,14 +31,19 @@ __global__ __launch_bounds__(256) void probe_dequant(const uint32_t *w, q4::u32x
 
 // The block dot of the order as the kernels run it: for lane data a (A
 // operand) and one packed code word w per lane, D = MFMA(a, dequant(w)) and
-// E = MFMA(a, V + 8); both are returned, [waves][64][4] each.
+// (bf16) E = MFMA(a, 24) or (fp16, no correction) E = 0; both are returned,
+// [waves][64][4] each.
 template <bool BF16>
 __global__ __launch_bounds__(64) void probe_q4dot(const q4::u32x4 *a, const uint32_t *w, q4::f32x4 *d,
                                                   q4::f32x4 *e)
 {
     const int i = blockIdx.x * 64 + threadIdx.x;
-    d[i] = q4::blockdot<BF16>(a[i], q4::Dequant<BF16>()(w[i]));
-    e[i] = q4::blockdot<BF16>(a[i], q4::Dequant<BF16>().offset);
+    const q4::Dequant<BF16> dq;
+    d[i] = q4::blockdot<BF16>(a[i], dq(w[i]));
+    if constexpr (q4::kCorrected<BF16>)
+        e[i] = q4::blockdot<BF16>(a[i], dq.offset);
+    else
+        e[i] = (q4::f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
 // fmaf(d, s, +0) on the VALU, for the single-rounding check of the scale step.

@@ -57,6 +57,17 @@ SET_7B = (
 LM_HEAD_7B = Matrix("lm_head", 152064, 3584)
 N_LAYERS_7B = 28
 
+# GPT-2-small-shaped attention projections ("Why LLM Decoding Is Slow, and
+# Why Batching Is (Almost) Free", section "The Catch: Every User Brings Their
+# Own Cache": 12 heads of 64, d_model 768).  The MLP and vocabulary widths
+# are not on the pages, so only the 768-wide projections are built.
+SET_GPT2 = (
+    Matrix("q_proj", 768, 768),
+    Matrix("k_proj", 768, 768),
+    Matrix("v_proj", 768, 768),
+    Matrix("o_proj", 768, 768),
+)
+
 # The workloads.  x dtype: "f16" or "bf16".
 WORKLOADS = {
     1: dict(name="q4_matvec_896", matrices=(Matrix("w", 896, 896),), Ms=(1,), x="f16"),
@@ -65,6 +76,7 @@ WORKLOADS = {
     4: dict(name="qwen2.5-7b_layer_set_mixed_124", matrices=SET_7B, Ms=(124,), x="bf16"),
     5: dict(name="qwen2.5-7b_decode_weight_stream", matrices=SET_7B + (LM_HEAD_7B,),
             Ms=(1, 4, 16, 64), x="bf16"),
+    6: dict(name="gpt2-small_attention_set", matrices=SET_GPT2, Ms=tuple(range(1, 17)), x="bf16"),
 }
 
 

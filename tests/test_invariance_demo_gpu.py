@@ -23,6 +23,8 @@ import pytest
 import torch
 
 import bit_quantized_matmul_q4_amd as q4
+import oracle
+import synth
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -71,10 +73,19 @@ def test_tied_pairs_exact_and_library_invariant():
     w = q4.pack(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
     xd = x.cuda()
     alone = q4.linear(xd[:1], w, kernel="auto")[0]      # one row: matrix-vector kernel
-    batched = q4.linear(xd, w, kernel="auto")[0]        # 124 rows: matrix-matrix kernel
+    batch = q4.linear(xd, w, kernel="auto")             # 124 rows: matrix-matrix kernel
+    batched = batch[0]
     assert q4.get_crossover() < 124
     assert torch.equal(alone.view(torch.int32), batched.view(torch.int32)), "cache write differs"
     assert torch.equal(winners(alone), winners(batched))
+
+    # every one of the library's logits, alone and in the batch, against the oracle
+    x_bits = x.view(torch.int16).numpy().view(np.uint16)
+    y_ref, a_ref = oracle.linear(x_bits, True, oracle.pack(codes), scales.view(np.uint16))
+    assert oracle.max_normalised_error(alone.cpu().numpy()[None, :], y_ref[:1], a_ref[:1]) <= gu.TOL
+    assert oracle.max_normalised_error(batch.cpu().numpy(), y_ref, a_ref) <= gu.TOL
+    # the tied pairs are exact ties for the oracle too (fp64 sums of the same terms)
+    assert np.array_equal(y_ref[0, 0::2], y_ref[0, 1::2])
 
     # the contrast: two plain kernels with different summation orders
     wdev = torch.from_numpy(wd.astype(np.float32)).cuda()  # dequantized weights, exact in fp32
@@ -86,3 +97,77 @@ def test_tied_pairs_exact_and_library_invariant():
     gu.note("contrast kernels: %d of %d cached values differ, %d of %d tied choices flip"
             % (differ, gemv_like.numel(), flips, gemv_like.numel() // 2))
     assert differ > 0 and flips > 0, "the contrast kernels happened to agree; the demonstration needs a new seed"
+
+
+def test_cache_carries_over_steps():
+    """Two decode steps, as the page traces it ("The Other Request Already
+    Finished"): step 1 runs a 124-row batch (120 prefill rows + 4 verify
+    rows) through W1 and writes its outputs, rounded to bf16, into a cache;
+    step 2 runs the 4 verify requests' cached rows through W2 in one 4-row
+    call.  Served one request at a time instead (one row per call at both
+    steps), the library writes the same cache and returns the same step-2
+    outputs, bit for bit.  Both steps match the oracle: step 2's oracle
+    input is the oracle's own step-1 output rounded the same way (fp32, then
+    bf16); where that rounding lands on the other side of a bf16 boundary
+    than the library's, the few differing cache entries (at most one bf16
+    step each) widen step 2's bound by exactly their contribution.  Two
+    plain kernels with different summation orders, used the same way, write
+    caches that differ and carry the difference into step 2."""
+    K1, N1, N2 = 3584, 1024, 512  # W1: [N1, K1]; the cache row feeds W2: [N2, N1]
+    M, V = 124, 4
+    x1 = synth.activations(M, K1, "bf16", workload=7, matrix=0)
+    c1, s1 = synth.codes(N1, K1, 7, 1), synth.scales(N1, K1, 7, 1)
+    c2, s2 = synth.codes(N2, N1, 7, 2), synth.scales(N2, N1, 7, 2)
+    w1, w2 = gu.pack_dev(c1, s1), gu.pack_dev(c2, s2)
+    xd = gu.x_to_dev(x1, True)
+    gu.note("cache demo: step 1 batched (M=%d), step 2 (M=%d)" % (M, V))
+    y1 = q4.linear(xd, w1)                                     # matrix-matrix kernel
+    cache = y1[M - V:].to(torch.bfloat16)                      # the verify rows' cache entries
+    y2 = q4.linear(cache, w2)                                  # one 4-row call
+    gu.note("cache demo: one request at a time")
+    alone_cache, alone_y2 = [], []
+    for r in range(V):
+        y1r = q4.linear(xd[M - V + r:M - V + r + 1], w1)      # matrix-vector kernel
+        cr = y1r.to(torch.bfloat16)
+        alone_cache.append(cr)
+        alone_y2.append(q4.linear(cr, w2))
+    alone_cache, alone_y2 = torch.cat(alone_cache), torch.cat(alone_y2)
+    assert torch.equal(cache.view(torch.int16), alone_cache.view(torch.int16)), "cache entries differ"
+    assert torch.equal(y2.view(torch.int32), alone_y2.view(torch.int32)), "step-2 outputs differ"
+
+    # step 1 against the oracle
+    y1_ref, a1_ref = oracle.linear(x1, True, oracle.pack(c1), s1)
+    assert oracle.max_normalised_error(y1.cpu().numpy(), y1_ref, a1_ref) <= gu.TOL
+    # the oracle's cache: its step-1 values rounded to fp32, then to bf16
+    cache_ref = synth.f64_to_bf16_bits(y1_ref[M - V:])
+    cache_gpu = cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    cref64 = (cache_ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    cgpu64 = (cache_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    diff = cache_ref != cache_gpu
+    assert diff.sum() <= max(1, cache_ref.size // 1000), int(diff.sum())
+    steps = np.abs(cgpu64 - cref64)
+    ulp = np.abs(cref64) * 2.0 ** -7
+    assert np.all(steps[diff] <= ulp[diff] * 1.0000001 + 1e-45), "a cache entry differs by more than one bf16 step"
+    # step 2 against the oracle on the oracle's cache
+    y2_ref, a2_ref = oracle.linear(cache_ref, True, oracle.pack(c2), s2)
+    wabs = np.abs((c2.astype(np.float64) - 8.0) * np.repeat(gu.f16_bits_to_f64(s2), 32, axis=1))  # [N2, N1]
+    widen = steps @ wabs.T                                    # [V, N2]: the differing entries' share
+    err = np.abs(y2.cpu().numpy().astype(np.float64) - y2_ref)
+    assert np.all(err <= gu.TOL * a2_ref + widen)
+
+    # the contrast: per-row reduction (one request alone) against a dense
+    # product over the batch, both in fp32 on the dequantized weights
+    w1d = torch.from_numpy(((c1.astype(np.float64) - 8) * np.repeat(gu.f16_bits_to_f64(s1), 32, axis=1))
+                           .astype(np.float32)).cuda()
+    w2d = torch.from_numpy(((c2.astype(np.float64) - 8) * np.repeat(gu.f16_bits_to_f64(s2), 32, axis=1))
+                           .astype(np.float32)).cuda()
+    xf = xd.float()
+    row_cache = torch.stack([(xf[M - V + r:M - V + r + 1] * w1d).sum(dim=1) for r in range(V)]).to(torch.bfloat16)
+    mm_cache = torch.mm(xf, w1d.t().contiguous())[M - V:].to(torch.bfloat16)
+    cache_differ = int((row_cache.view(torch.int16) != mm_cache.view(torch.int16)).sum())
+    y2_row = torch.mm(row_cache.float(), w2d.t().contiguous())
+    y2_mm = torch.mm(mm_cache.float(), w2d.t().contiguous())
+    out_differ = int((y2_row.view(torch.int32) != y2_mm.view(torch.int32)).sum())
+    gu.note("contrast kernels: %d of %d cache entries differ, %d of %d step-2 outputs differ"
+            % (cache_differ, row_cache.numel(), out_differ, y2_row.numel()))
+    assert cache_differ > 0 and out_differ > 0

@@ -6,12 +6,15 @@
   which is what lets a row's bits ignore M and the other rows;
 * run-to-run determinism;
 * exactness when every partial sum is representable;
-* the nibble dequantization gives the operand V + q (V = 128 in bf16, 1024
-  in fp16) exactly for every code at every position of a packed word;
-* the corrected block dot: D = MFMA(x, V + q) is the plain MFMA of the
-  dequantized operand, E = MFMA(x, V + 8) is the same for every column,
+* the nibble dequantization gives the operand exactly for every code at
+  every position of a packed word: 16 + q in bf16, q - 8 in fp16;
+* the bf16 corrected block dot: D = MFMA(x, 16 + q) is the plain MFMA of
+  the dequantized operand, E = MFMA(x, 24) is the same for every column,
   D == E for a block of all-8 codes, and fl(D - E) is within the fp32
   accumulation bound of the exact sum of x (q - 8);
+* the fp16 block dot D = MFMA(x, q - 8) is within the fp32 accumulation
+  bound of the exact sum relative to sum |x (q - 8)| (zero weights add
+  exactly nothing), and a block with one non-zero weight is exact;
 * fmaf(d, s, 0) is the single-rounded product (no flush of subnormals).
 """
 import numpy as np
@@ -129,8 +132,22 @@ def test_mfma_slot_invariance_and_determinism(probe, bf16):
     assert np.all(D4[:, 1:, :] == 0)
 
 
-MAGIC = {True: 0x4300, False: 0x6400}  # V = 128 (bf16), 1024 (fp16)
 SHIFTS = (4 * (np.arange(8) // 2) + 16 * (np.arange(8) % 2)).astype(np.uint32)  # code r's bit
+
+
+def operand_bits(q: np.ndarray, bf16: bool) -> np.ndarray:
+    """The B operand the order defines for codes q: 16 + q (bf16), q - 8 (fp16)."""
+    q = np.asarray(q, np.int64)
+    return enc(q + 16.0, True) if bf16 else enc(q - 8.0, False)
+
+
+def lane_words(q: np.ndarray) -> np.ndarray:
+    """Codes [w, 32, 16] (k, column) -> one packed word per lane [w, 64]:
+    lane l = 16 g + c holds column c, k = 8 g + r, code r at SHIFTS[r]."""
+    l = np.arange(64)
+    ks = (8 * (l // 16))[:, None] + np.arange(8)[None, :]
+    lane_codes = q[:, ks, (l % 16)[:, None]].astype(np.uint32)  # [w, 64, 8]
+    return (lane_codes << SHIFTS).sum(axis=-1, dtype=np.uint32)
 
 
 @pytest.mark.parametrize("bf16", [True, False])
@@ -141,43 +158,68 @@ def test_dequant_every_code_every_position(probe, bf16):
                             rng.integers(0, 1 << 32, size=4096, dtype=np.uint64)]).astype(np.uint32)
     got = probe.dequant(words, bf16)
     codes = (words[:, None] >> SHIFTS[None, :]) & 0xF
-    base = 128.0 if bf16 else 1024.0
-    expect = enc(codes.astype(np.float64) + base, bf16)
-    assert np.array_equal(got, expect)
-    assert np.array_equal(got, (MAGIC[bf16] | codes).astype(np.uint16))
+    assert np.array_equal(got, operand_bits(codes, bf16))
+    if bf16:  # the pattern itself: 16 with the code in the top mantissa bits
+        assert np.array_equal(got, (0x4180 | (codes << 3)).astype(np.uint16))
 
 
-@pytest.mark.parametrize("bf16", [True, False])
-def test_corrected_block_dot(probe, bf16):
-    gu.note("corrected block dot bf16=%s" % bf16)
+def test_corrected_block_dot_bf16(probe):
+    gu.note("corrected block dot bf16")
     rng = np.random.default_rng(16)
     w = 96
     xv = rng.normal(0, 1, size=(w, 16, 32)) * np.exp(rng.normal(0, 1.5, size=(w, 16, 1)))
-    A = enc(xv, bf16)
+    A = enc(xv, True)
     q = rng.integers(0, 16, size=(w, 32, 16)).astype(np.uint32)
     q[:16] = 8  # all-8 blocks
-    # lane l = 16 g + c: codes of column c, k = 8 g + r, packed into one word
-    l = np.arange(64)
-    ks = (8 * (l // 16))[:, None] + np.arange(8)[None, :]
-    lane_codes = q[:, ks, (l % 16)[:, None]]  # [w, 64, 8]
-    words = (lane_codes << SHIFTS).sum(axis=-1, dtype=np.uint32)
-    Bv = (MAGIC[bf16] | q).astype(np.uint16)
-    a4, b4 = to_lanes(A, Bv)
-    D, E = probe.q4dot(a4, words, bf16)
+    a4, b4 = to_lanes(A, operand_bits(q, True))
+    D, E = probe.q4dot(a4, lane_words(q), True)
     # D is the plain MFMA of the dequantized operand
-    assert np.array_equal(D.view(np.uint32), probe.mfma(a4, b4, bf16).view(np.uint32))
+    assert np.array_equal(D.view(np.uint32), probe.mfma(a4, b4, True).view(np.uint32))
     Dm, Em = from_lanes(D), from_lanes(E)
-    # E depends on the row only
+    # E depends on the row only, and is the MFMA against 24 everywhere
     assert np.array_equal(Em.view(np.uint32), np.repeat(Em[:, :, :1], 16, axis=2).view(np.uint32))
+    _, b24 = to_lanes(A, np.full((w, 32, 16), enc(np.array([24.0]), True)[0], np.uint16))
+    assert np.array_equal(E.view(np.uint32), probe.mfma(a4, b24, True).view(np.uint32))
     # a block of all-8 codes: D == E, so the block dot is exactly zero
     assert np.array_equal(Dm[:16].view(np.uint32), Em[:16].view(np.uint32))
-    # fl(D - E) against the exact sum, within the fp32 bound for D and E
-    xd = dec(A, bf16)
+    # fl(D - E) against the exact sum: each of D and E is a sum of 32 exact
+    # products (operands at most 31 and 24), so within 33 u of their sums of
+    # magnitudes, plus the subtraction's own rounding
+    xd = dec(A, True)
     s = (Dm - Em).astype(np.float32).astype(np.float64)
     exact = np.einsum("wmk,wkn->wmn", xd, q.astype(np.float64) - 8.0)
-    V = 128.0 if bf16 else 1024.0
-    bound = 2 * 33 * 2.0 ** -24 * (V + 15.0) * np.abs(xd).sum(axis=2)[:, :, None]
+    u = 2.0 ** -24
+    bound = 33 * u * (31.0 + 24.0) * np.abs(xd).sum(axis=2)[:, :, None] + u * np.abs(exact)
     assert np.all(np.abs(s - exact) <= bound)
+
+
+def test_exact_operand_block_dot_f16(probe):
+    gu.note("exact-operand block dot fp16")
+    rng = np.random.default_rng(17)
+    w = 128
+    # wide-ranging same-sign and mixed-sign activations
+    xv = rng.uniform(1.0, 4000.0, size=(w, 16, 32)) * np.where(rng.random((w, 16, 1)) < 0.5, 1.0, -1.0)
+    xv[w // 2:] *= np.where(rng.random((w // 2, 16, 32)) < 0.5, 1.0, -1.0)
+    A = enc(xv, False)
+    q = rng.integers(0, 16, size=(w, 32, 16)).astype(np.uint32)
+    # a quarter of the blocks: codes 8 except one 7 or 9 (one non-zero weight)
+    sp = slice(0, w // 4)
+    q[sp] = 8
+    kk = rng.integers(0, 32, size=(w // 4, 16))
+    q[sp][np.arange(w // 4)[:, None], kk, np.arange(16)[None, :]] = rng.choice([7, 9], size=(w // 4, 16))
+    a4, b4 = to_lanes(A, operand_bits(q, False))
+    D, E = probe.q4dot(a4, lane_words(q), False)
+    assert np.array_equal(D.view(np.uint32), probe.mfma(a4, b4, False).view(np.uint32))
+    assert np.all(E == 0)  # no correction in fp16
+    Dm = from_lanes(D).astype(np.float64)
+    xd = dec(A, False)
+    wq = q.astype(np.float64) - 8.0
+    exact = np.einsum("wmk,wkn->wmn", xd, wq)
+    mag = np.einsum("wmk,wkn->wmn", np.abs(xd), np.abs(wq))
+    # one non-zero weight: the single exact product, exactly
+    assert np.array_equal(Dm[sp], exact[sp])
+    # otherwise within 33 u of the sum of the products' magnitudes
+    assert np.all(np.abs(Dm - exact) <= 33 * 2.0 ** -24 * mag)
 
 
 def test_fma0_single_rounding(probe):
