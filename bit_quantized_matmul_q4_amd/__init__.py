@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import KERNELS, Q4Error
 
-__all__ = ["Q4Weight", "linear", "pack", "quantize", "quantize_pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
+__all__ = ["Q4Weight", "linear", "linear_noalloc", "pack", "quantize", "quantize_pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
            "set_crossover", "segments", "Q4Error", "library_path"]
 
 
@@ -164,6 +164,34 @@ def linear(x: torch.Tensor, w: Q4Weight, out: torch.Tensor | None = None, kernel
         st = lib.q4_linear_ex(x.data_ptr(), dtype, w.codes.data_ptr(), w.scales.data_ptr(), out.data_ptr(),
                               M, N, K, KERNELS[kernel], ws_ptr, ws_len, _stream(dev))
     _lib.check(st, "q4_linear_ex")
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, w: Q4Weight, out: torch.Tensor, kernel: str = "auto") -> torch.Tensor:
+    """q4_linear_noalloc: like ``linear`` with the library's fixed scratch
+    buffer as the workspace, so the call allocates nothing (``out`` must be
+    given).  Calls that overlap in time on one GPU share that buffer and
+    race."""
+    lib = _lib.load()
+    _need(x, "x", (torch.bfloat16, torch.float16), 2)
+    dev = x.device
+    if not isinstance(w, Q4Weight):
+        raise TypeError("w must be a Q4Weight (see pack)")
+    _need(w.codes, "w.codes", (torch.uint8,), 1, dev)
+    _need(w.scales, "w.scales", (torch.float16,), 1, dev)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    _need(out, "out", (torch.float32,), 2, dev)
+    if tuple(out.shape) != (M, w.N):
+        raise ValueError("out must be [%d, %d]" % (M, w.N))
+    if kernel not in KERNELS:
+        raise ValueError("kernel must be one of %s" % sorted(KERNELS))
+    dtype = _lib.Q4_BF16 if x.dtype == torch.bfloat16 else _lib.Q4_F16
+    with torch.cuda.device(dev):
+        st = lib.q4_linear_noalloc(x.data_ptr(), dtype, w.codes.data_ptr(), w.scales.data_ptr(), out.data_ptr(),
+                                   M, w.N, K, KERNELS[kernel], _stream(dev))
+    _lib.check(st, "q4_linear_noalloc")
     return out
 
 

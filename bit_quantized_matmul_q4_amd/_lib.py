@@ -20,6 +20,7 @@ Q4_ERR_ALIGN = -3
 Q4_ERR_ENUM = -4
 Q4_ERR_HIP = -5
 Q4_ERR_WORKSPACE = -6
+Q4_ERR_SCRATCH = -7
 
 Q4_F16 = 0
 Q4_BF16 = 1
@@ -32,13 +33,13 @@ Q4_GEMM = 2
 KERNELS = {"auto": Q4_AUTO, "gemv": Q4_GEMV, "gemm": Q4_GEMM}
 
 EXPORTS = (
-    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_workspace_bytes", "q4_pack", "q4_quantize",
+    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_linear_noalloc", "q4_workspace_bytes", "q4_pack", "q4_quantize",
     "q4_packed_code_bytes", "q4_packed_scale_bytes",
     "q4_get_crossover", "q4_set_crossover", "q4_segments", "q4_strerror",
     "q4_last_hip_error", "q4_abi_version",
 )
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class Q4Error(RuntimeError):
@@ -63,6 +64,8 @@ def _declare(lib):
     lib.q4_linear_f16.restype = i
     lib.q4_linear_ex.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.q4_linear_ex.restype = i
+    lib.q4_linear_noalloc.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
+    lib.q4_linear_noalloc.restype = i
     lib.q4_workspace_bytes.argtypes = [i, i, i, i]
     lib.q4_workspace_bytes.restype = sz
     lib.q4_pack.argtypes = [vp, vp, vp, vp, i, i, vp]

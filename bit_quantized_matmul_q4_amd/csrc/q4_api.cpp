@@ -114,6 +114,7 @@ const char *q4_strerror(int status)
     case Q4_ERR_ENUM: return "unknown dtype or kernel selector";
     case Q4_ERR_HIP: return "HIP launch error (see q4_last_hip_error)";
     case Q4_ERR_WORKSPACE: return "workspace_bytes > 0 with a NULL workspace";
+    case Q4_ERR_SCRATCH: return "the call needs more than the library's fixed scratch buffer (Q4_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -160,9 +161,11 @@ size_t q4_workspace_bytes(int M, int N, int K, int kernel)
     return q4::gemm_workspace_bytes(M, N, K);
 }
 
-int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales, float *y,
-                 int M, int N, int K, int kernel, void *workspace, size_t workspace_bytes,
-                 void *stream)
+// The checks and dispatch shared by q4_linear_ex and q4_linear_noalloc.
+// scratch: take the library's fixed device buffer as the workspace (the
+// caller passes none).
+static int linear_impl(const void *x, int x_dtype, const void *Wq, const void *scales, float *y, int M, int N,
+                       int K, int kernel, void *workspace, size_t workspace_bytes, bool scratch, void *stream)
 {
     if (!x || !Wq || !scales || !y)
         return Q4_ERR_NULL;
@@ -180,9 +183,20 @@ int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
     if (workspace && !aligned(workspace, 256))
         return Q4_ERR_ALIGN;
 
+    const size_t need = q4::gemm_workspace_bytes(M, N, K);
     const int k = kernel == Q4_AUTO
-                      ? auto_kernel(M, K, workspace_bytes >= q4::gemm_workspace_bytes(M, N, K))
+                      ? auto_kernel(M, K, scratch ? need <= q4::kScratchBytes : workspace_bytes >= need)
                       : kernel;
+    if (k == Q4_GEMM && scratch) {
+        if (need > q4::kScratchBytes)
+            return Q4_ERR_SCRATCH;
+        if (need > 0) {
+            const int st = hip_status(q4::scratch_buffer(&workspace));
+            if (st != Q4_OK)
+                return st;
+            workspace_bytes = need;
+        }
+    }
 
     const bool bf16 = x_dtype == Q4_BF16;
     hipStream_t s = (hipStream_t)stream;
@@ -191,6 +205,19 @@ int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
                                           M, N, K, s));
     return hip_status(q4::launch_gemm(x, bf16, (const uint8_t *)Wq, (const uint16_t *)scales, y, M, N,
                                       K, workspace_bytes ? workspace : nullptr, workspace_bytes, s));
+}
+
+int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales, float *y,
+                 int M, int N, int K, int kernel, void *workspace, size_t workspace_bytes,
+                 void *stream)
+{
+    return linear_impl(x, x_dtype, Wq, scales, y, M, N, K, kernel, workspace, workspace_bytes, false, stream);
+}
+
+int q4_linear_noalloc(const void *x, int x_dtype, const void *Wq, const void *scales, float *y, int M, int N,
+                      int K, int kernel, void *stream)
+{
+    return linear_impl(x, x_dtype, Wq, scales, y, M, N, K, kernel, nullptr, 0, true, stream);
 }
 
 int q4_linear(const void *x, const void *Wq, const void *scales, float *y, int M, int N, int K,

@@ -37,6 +37,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
@@ -1578,6 +1580,49 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
     hipLaunchKernelGGL(q4_tree_combine, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
                        (const float *)workspace, y, mn, gk);
     return hipGetLastError();
+}
+
+// ================================================================ scratch
+// A fixed device buffer for callers that cannot allocate (code under graph
+// capture, tight serving loops): it holds the matrix-matrix kernel's K-split
+// partials, which no call needs more than 4 MiB of (the split stops doubling
+// once the grid reaches the compute units: fewer than 512 column unit x row
+// unit x split workgroups, each unit at most 32 rows by 64 columns, so at
+// most 4 x 2048 x 512 bytes).  Each device holds its own copy until the
+// process ends; its device address is looked up once per device (the
+// array's name is only a host-side stand-in).  Every call on a device shares
+// it and leaves the last call's partials in it (each call writes every
+// partial it reads, so nothing needs clearing); calls that overlap on one
+// device race.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_buffer(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+            if (e != hipSuccess)
+                return e;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_quantize(const void *w, int kind, uint8_t *codes, uint16_t *scales, int N, int K,

@@ -21,6 +21,12 @@ hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16
 // Bytes of workspace the matrix-matrix kernel can use for this shape.
 size_t gemm_workspace_bytes(int M, int N, int K);
 
+// The library's fixed per-device scratch buffer (for the entry point that
+// allocates nothing): its size, and its device address on the current device
+// (looked up once per device).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+hipError_t scratch_buffer(void **ptr);
+
 // Canonical codes [N][K] and scales [N][K/32] -> the tiled layout.
 hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales_in, uint8_t *wq, uint16_t *scales_out,
                        int N, int K, hipStream_t stream);

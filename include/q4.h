@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 4
+#define Q4_ABI_VERSION 5
 
 enum q4_status {
     Q4_OK = 0,
@@ -67,8 +67,12 @@ enum q4_status {
     Q4_ERR_ALIGN = -3,     /* a pointer below the alignment its call states */
     Q4_ERR_ENUM = -4,      /* unknown dtype or kernel selector */
     Q4_ERR_HIP = -5,       /* a HIP call failed (see q4_last_hip_error) */
-    Q4_ERR_WORKSPACE = -6  /* workspace_bytes non-zero with a NULL workspace */
+    Q4_ERR_WORKSPACE = -6, /* workspace_bytes non-zero with a NULL workspace */
+    Q4_ERR_SCRATCH = -7    /* the call needs more than Q4_SCRATCH_BYTES of scratch */
 };
+
+/* Size of the fixed per-device scratch buffer q4_linear_noalloc uses. */
+#define Q4_SCRATCH_BYTES (4u << 20)
 
 enum q4_dtype { Q4_F16 = 0, Q4_BF16 = 1, Q4_F32 = 2 /* q4_quantize input only */ };
 
@@ -105,6 +109,24 @@ int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y,
 int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
                  float *y, int M, int N, int K, int kernel,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * q4_linear_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the call allocates nothing.  Where the
+ * matrix-matrix kernel splits K it keeps its partial results in the
+ * library's fixed scratch buffer, a static device array of Q4_SCRATCH_BYTES
+ * bytes per GPU that lives until the process ends; every need of the current
+ * kernels is below that (Q4_ERR_SCRATCH otherwise, before any launch).  The
+ * buffer's device address is looked up on the first such call on each
+ * device (with that device current).  All calls on one GPU share the buffer
+ * and leave their partials in it; two calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * Same arguments, results and errors as q4_linear_ex otherwise; the bits
+ * equal q4_linear_ex's with a workspace.
+ */
+int q4_linear_noalloc(const void *x, int x_dtype, const void *Wq, const void *scales,
+                      float *y, int M, int N, int K, int kernel, void *stream);
 
 /* Workspace bytes that q4_linear_ex can use for this shape and kernel
  * (0 if the kernel uses none).  Pure host computation; 0 for bad shapes. */

@@ -38,8 +38,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_and_strerror(lib):
-    assert lib.q4_abi_version() == 4
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    assert lib.q4_abi_version() == 5
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
     assert lib.q4_strerror(-99) == b"unknown status"
     assert lib.q4_last_hip_error() == 0
@@ -174,3 +174,31 @@ def test_argument_checks(lib):
     assert q(FAKE, _lib.Q4_F32, FAKE + 8, FAKE, 4, 64, None) == _lib.Q4_ERR_ALIGN
     assert q(FAKE, _lib.Q4_F32, FAKE, FAKE + 1, 4, 64, None) == _lib.Q4_ERR_ALIGN
     assert lib.q4_last_hip_error() == 0
+
+
+SCRATCH_BYTES = 4 << 20  # Q4_SCRATCH_BYTES
+
+
+def test_scratch_covers_every_workspace_need(lib):
+    """The fixed scratch buffer of q4_linear_noalloc holds the workspace the
+    matrix-matrix kernel asks for at every shape of a wide sweep (so the
+    entry point's size check never fires for the current kernels)."""
+    worst = 0
+    for K in (32, 64, 128, 256, 512, 768, 896, 1024, 2048, 3584, 4864, 8192, 8224, 18944, 32768):
+        for N in list(range(1, 2100, 37)) + [2304, 3263, 3584, 4096, 4864, 18944, 37888, 152064]:
+            for M in list(range(1, 260, 3)) + [512, 1024, 4096]:
+                for kernel in (0, 2):
+                    worst = max(worst, lib.q4_workspace_bytes(M, N, K, kernel))
+    assert 0 < worst <= SCRATCH_BYTES, worst
+
+
+def test_noalloc_argument_checks(lib):
+    """q4_linear_noalloc rejects bad arguments before any HIP call."""
+    p = ctypes.c_void_p(4096)
+    y = ctypes.c_void_p(4096)
+    assert lib.q4_linear_noalloc(None, 1, p, p, y, 1, 16, 32, 0, None) == -1
+    assert lib.q4_linear_noalloc(p, 7, p, p, y, 1, 16, 32, 0, None) == -4
+    assert lib.q4_linear_noalloc(p, 1, p, p, y, 1, 16, 32, 9, None) == -4
+    assert lib.q4_linear_noalloc(p, 1, p, p, y, 0, 16, 32, 0, None) == -2
+    assert lib.q4_linear_noalloc(p, 1, p, p, y, 1, 16, 48, 0, None) == -2
+    assert lib.q4_linear_noalloc(ctypes.c_void_p(4104), 1, p, p, y, 1, 16, 32, 0, None) == -3
