@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import KERNELS, Q4Error
 
-__all__ = ["Q4Weight", "linear", "linear_noalloc", "pack", "quantize", "quantize_pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
+__all__ = ["Q4Weight", "linear", "linear_noalloc", "linear_grouped", "pack", "pack_nibbles", "quantize", "quantize_pack", "concat_n", "split_n", "packed_sizes", "workspace_bytes", "get_crossover",
            "set_crossover", "segments", "Q4Error", "library_path"]
 
 
@@ -89,6 +89,26 @@ def pack(codes: torch.Tensor, scales: torch.Tensor) -> Q4Weight:
     with torch.cuda.device(dev):
         st = lib.q4_pack(codes.data_ptr(), scales.data_ptr(), wq.data_ptr(), ws.data_ptr(), N, K, _stream(dev))
     _lib.check(st, "q4_pack")
+    return Q4Weight(wq, ws, N, K)
+
+
+def pack_nibbles(rows: torch.Tensor, scales: torch.Tensor) -> Q4Weight:
+    """Nibble rows uint8 [N, K/2] (byte j: k = 2j low nibble, 2j + 1 high),
+    scales float16 [N, K/32] -> Q4Weight (q4_pack_nibbles)."""
+    lib = _lib.load()
+    _need(rows, "rows", (torch.uint8,), 2)
+    dev = rows.device
+    _need(scales, "scales", (torch.float16,), 2, dev)
+    N, K = rows.shape[0], rows.shape[1] * 2
+    if tuple(scales.shape) != (N, K // 32):
+        raise ValueError("scales must be [%d, %d]" % (N, K // 32))
+    cb, sb = packed_sizes(N, K)
+    wq = torch.empty(cb, dtype=torch.uint8, device=dev)
+    ws = torch.empty(sb // 2, dtype=torch.float16, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.q4_pack_nibbles(rows.data_ptr(), scales.data_ptr(), wq.data_ptr(), ws.data_ptr(), N, K,
+                                 _stream(dev))
+    _lib.check(st, "q4_pack_nibbles")
     return Q4Weight(wq, ws, N, K)
 
 
@@ -193,6 +213,44 @@ def linear_noalloc(x: torch.Tensor, w: Q4Weight, out: torch.Tensor, kernel: str 
                                    M, w.N, K, KERNELS[kernel], _stream(dev))
     _lib.check(st, "q4_linear_noalloc")
     return out
+
+
+def linear_grouped(x: torch.Tensor, weights, outs=None) -> list:
+    """q4_linear_grouped: y_i = x . dequant(w_i)^T for 1..8 weights sharing
+    x's K, in one launch where the matrix-vector kernel's segment form
+    applies.  Returns the outputs (allocated unless ``outs`` is given)."""
+    lib = _lib.load()
+    _need(x, "x", (torch.bfloat16, torch.float16), 2)
+    dev = x.device
+    weights = list(weights)
+    if not 1 <= len(weights) <= _lib.GROUP_MAX:
+        raise ValueError("linear_grouped takes 1..%d weights" % _lib.GROUP_MAX)
+    M, K = x.shape
+    if outs is None:
+        outs = [torch.empty((M, w.N), dtype=torch.float32, device=dev) for w in weights]
+    outs = list(outs)
+    if len(outs) != len(weights):
+        raise ValueError("one output per weight")
+    items = (_lib.GroupItem * len(weights))()
+    for i, (w, y) in enumerate(zip(weights, outs)):
+        if not isinstance(w, Q4Weight):
+            raise TypeError("weights must be Q4Weight objects")
+        if w.K != K:
+            raise ValueError("weight %d has K=%d, x has K=%d" % (i, w.K, K))
+        _need(w.codes, "w.codes", (torch.uint8,), 1, dev)
+        _need(w.scales, "w.scales", (torch.float16,), 1, dev)
+        cb, sb = packed_sizes(w.N, K)
+        if w.codes.numel() != cb or w.scales.numel() * 2 != sb:
+            raise ValueError("packed weight %d sizes do not match N=%d K=%d" % (i, w.N, K))
+        _need(y, "out", (torch.float32,), 2, dev)
+        if tuple(y.shape) != (M, w.N):
+            raise ValueError("out %d must be [%d, %d]" % (i, M, w.N))
+        items[i] = _lib.GroupItem(w.codes.data_ptr(), w.scales.data_ptr(), y.data_ptr(), w.N)
+    dtype = _lib.Q4_BF16 if x.dtype == torch.bfloat16 else _lib.Q4_F16
+    with torch.cuda.device(dev):
+        st = lib.q4_linear_grouped(x.data_ptr(), dtype, items, len(weights), M, K, _stream(dev))
+    _lib.check(st, "q4_linear_grouped")
+    return outs
 
 
 def get_crossover() -> int:

@@ -33,13 +33,20 @@ Q4_GEMM = 2
 KERNELS = {"auto": Q4_AUTO, "gemv": Q4_GEMV, "gemm": Q4_GEMM}
 
 EXPORTS = (
-    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_linear_noalloc", "q4_workspace_bytes", "q4_pack", "q4_quantize",
+    "q4_linear", "q4_linear_f16", "q4_linear_ex", "q4_linear_noalloc", "q4_linear_grouped", "q4_workspace_bytes",
+    "q4_pack", "q4_pack_nibbles", "q4_quantize",
     "q4_packed_code_bytes", "q4_packed_scale_bytes",
     "q4_get_crossover", "q4_set_crossover", "q4_segments", "q4_strerror",
     "q4_last_hip_error", "q4_abi_version",
 )
 
-ABI_VERSION = 5
+ABI_VERSION = 6
+GROUP_MAX = 8
+
+
+class GroupItem(ctypes.Structure):
+    """q4_group_item (include/q4.h)."""
+    _fields_ = [("Wq", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int)]
 
 
 class Q4Error(RuntimeError):
@@ -66,6 +73,10 @@ def _declare(lib):
     lib.q4_linear_ex.restype = i
     lib.q4_linear_noalloc.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     lib.q4_linear_noalloc.restype = i
+    lib.q4_linear_grouped.argtypes = [vp, i, ctypes.POINTER(GroupItem), i, i, i, vp]
+    lib.q4_linear_grouped.restype = i
+    lib.q4_pack_nibbles.argtypes = [vp, vp, vp, vp, i, i, vp]
+    lib.q4_pack_nibbles.restype = i
     lib.q4_workspace_bytes.argtypes = [i, i, i, i]
     lib.q4_workspace_bytes.restype = sz
     lib.q4_pack.argtypes = [vp, vp, vp, vp, i, i, vp]

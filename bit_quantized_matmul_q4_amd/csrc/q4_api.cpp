@@ -261,8 +261,8 @@ int q4_quantize(const void *w, int w_dtype, uint8_t *codes, void *scales, int N,
     return hip_status(q4::launch_quantize(w, kind, codes, (uint16_t *)scales, N, K, (hipStream_t)stream));
 }
 
-int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
-            void *stream)
+static int pack_impl(const uint8_t *codes, bool nibbles, const void *scales, uint8_t *Wq, void *Wscales, int N,
+                     int K, void *stream)
 {
     if (!codes || !scales || !Wq || !Wscales)
         return Q4_ERR_NULL;
@@ -271,8 +271,61 @@ int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales
         return sh;
     if (!aligned(scales, 2) || !aligned(Wq, 16) || !aligned(Wscales, 8))
         return Q4_ERR_ALIGN;
-    return hip_status(q4::launch_pack(codes, (const uint16_t *)scales, Wq, (uint16_t *)Wscales, N, K,
+    return hip_status(q4::launch_pack(codes, nibbles, (const uint16_t *)scales, Wq, (uint16_t *)Wscales, N, K,
                                       (hipStream_t)stream));
+}
+
+int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
+            void *stream)
+{
+    return pack_impl(codes, false, scales, Wq, Wscales, N, K, stream);
+}
+
+int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
+                    void *stream)
+{
+    return pack_impl(Wq_rows, true, scales, Wq, Wscales, N, K, stream);
+}
+
+int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, int count, int M, int K,
+                      void *stream)
+{
+    if (!x || !items)
+        return Q4_ERR_NULL;
+    if (x_dtype != Q4_F16 && x_dtype != Q4_BF16)
+        return Q4_ERR_ENUM;
+    if (count < 1 || count > Q4_GROUP_MAX)
+        return Q4_ERR_SHAPE;
+    if (!aligned(x, 16))
+        return Q4_ERR_ALIGN;
+    q4::GroupItem g[Q4_GROUP_MAX];
+    for (int i = 0; i < count; ++i) {
+        const q4_group_item &it = items[i];
+        if (!it.Wq || !it.scales || !it.y)
+            return Q4_ERR_NULL;
+        const int sh = check_shape(M, it.N, K);
+        if (sh != Q4_OK)
+            return sh;
+        if (!aligned(it.Wq, 16) || !aligned(it.scales, 8) || !aligned(it.y, 4))
+            return Q4_ERR_ALIGN;
+        g[i] = q4::GroupItem{(const uint8_t *)it.Wq, (const uint16_t *)it.scales, it.y, it.N};
+    }
+    const bool bf16 = x_dtype == Q4_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    // one launch where the crossover rule picks the matrix-vector kernel and
+    // its segment form fits K; otherwise each matrix as q4_linear would run it
+    if (auto_kernel(M, K, false) == Q4_GEMV) {
+        hipError_t e = hipSuccess;
+        if (q4::launch_gemv_grouped(x, bf16, g, count, M, K, s, &e))
+            return hip_status(e);
+    }
+    for (int i = 0; i < count; ++i) {
+        const int st = linear_impl(x, x_dtype, g[i].wq, g[i].scales, g[i].y, M, g[i].N, K, Q4_AUTO, nullptr, 0,
+                                   false, stream);
+        if (st != Q4_OK)
+            return st;
+    }
+    return Q4_OK;
 }
 
 }  // extern "C"

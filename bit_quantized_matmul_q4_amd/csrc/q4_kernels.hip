@@ -524,7 +524,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // Ring positions are (tile i, quad q), q in [0, LQ); quads past the
 // segment's length are placeholders: their loads fall outside the
 // resources' ranges (zero, no memory access) and they compute nothing.
-// grid = (ceil(tiles / tpw), ceil(M / 16)), block = 1024.  With MR =
+// grid = (sum over the matrices of ceil(tiles / tpw), ceil(M / 16)),
+// block = 1024; a workgroup's matrix is the one whose range of workgroup
+// ids holds it (see SegItems).  With MR =
 // min(M, 16), dynamic LDS: roots [NB][TC][16 seg][MR][16] floats (NB = 1
 // if tpw <= TC: one combine after the last tile; else 2, double-buffered),
 // then outputs [tpw][MR][16] floats.
@@ -554,12 +556,21 @@ __device__ __forceinline__ void workgroup_barrier_lds()
     asm volatile("" ::: "memory");
 }
 
+// The matrices one launch of the segment form runs (one, or a group that
+// shares x, M and K): passed by value in the kernel arguments.
+constexpr int kGroupMax = 8;
+struct SegItems {
+    int count;
+    int wg_end[kGroupMax];  // workgroups (grid x) of matrices 0..i, cumulative
+    const uint8_t *wq[kGroupMax];
+    const uint16_t *scales[kGroupMax];
+    float *y[kGroupMax];
+    int N[kGroupMax];
+};
+
 template <bool BF16, int R, int LQ, bool SHORT, int TC>
-__global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x,
-                                                    const uint8_t *__restrict__ wq,
-                                                    const uint16_t *__restrict__ scales,
-                                                    float *__restrict__ y, int M, int N, int K, Plan plan,
-                                                    int tpw)
+__global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x, SegItems items, int M, int K,
+                                                    Plan plan, int tpw)
 {
     constexpr int D = seg_depth<R, LQ>();  // ring depth: a multiple of LQ
     static_assert(D % LQ == 0, "ring positions must map to fixed quads");
@@ -568,6 +579,28 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     float *roots = seg_lds;                                         // [NB][TC][16 seg][MR][16]
     float *ystage = seg_lds + seg_nbuf(TC, tpw) * TC * 16 * MR * 16;  // [tpw][MR][16]
 
+    // the workgroup's matrix (workgroups wg_end[i - 1] .. wg_end[i] - 1 run
+    // matrix i), chosen by selects on uniform values: an indexed read of the
+    // argument block could be copied to scratch memory
+    int it = 0;
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < items.count && (int)blockIdx.x >= items.wg_end[i - 1])
+            it = i;
+    const uint8_t *__restrict__ wq = items.wq[0];
+    const uint16_t *__restrict__ scales = items.scales[0];
+    float *__restrict__ y = items.y[0];
+    int N = items.N[0], wg0 = 0;
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i == it) {
+            wq = items.wq[i];
+            scales = items.scales[i];
+            y = items.y[i];
+            N = items.N[i];
+            wg0 = items.wg_end[i - 1];
+        }
+
     const int lane = threadIdx.x & 63;
     const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // segment
     const int g = lane >> 4, c = lane & 15;
@@ -575,7 +608,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     const int G = plan.G;
     const int m0 = blockIdx.y * 16;
     const int mrows = min(16, M - m0);
-    const int t_first = blockIdx.x * tpw;
+    const int t_first = ((int)blockIdx.x - wg0) * tpw;
     const int ntiles = min(tpw, n16 - t_first);
     const int qs = (j * G) >> 4;
     const int len = (((j + 1) * G) >> 4) - qs;  // 1 .. LQ quads
@@ -1129,7 +1162,10 @@ __global__ __launch_bounds__(256) void q4_quantize_kernel(const void *__restrict
 // One thread per (tile, quad, lane l = 16 g + c): gathers the four words of
 // lane l (codes of k = 32 b + 8 g + r, blocks b = 4q..4q+3 of column
 // 16t + c, code r at bit 4 (r / 2) + 16 (r % 2)) and, for g == 0, the
-// column's four scales.
+// column's four scales.  NIBBLES: the codes come as nibble rows [N][K/2]
+// (byte j of row n: k = 2j in bits 0..3, k = 2j + 1 in bits 4..7) instead of
+// one code per byte [N][K].
+template <bool NIBBLES>
 __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales_in,
                                                       uint8_t *__restrict__ wq,
@@ -1153,10 +1189,17 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict_
         const int b = 4 * q + i;
         uint32_t v = 0;
         if (n < N && b < nb) {
-            const uint8_t *src = codes + (size_t)n * K + 32 * b + 8 * g;
+            if constexpr (NIBBLES) {
+                const uint8_t *src = codes + (size_t)n * (K / 2) + 16 * b + 4 * g;
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                v |= (uint32_t)(src[r] & 0x0Fu) << (4 * (r / 2) + 16 * (r % 2));
+                for (int r = 0; r < 8; ++r)
+                    v |= (uint32_t)((src[r / 2] >> (4 * (r % 2))) & 0x0Fu) << (4 * (r / 2) + 16 * (r % 2));
+            } else {
+                const uint8_t *src = codes + (size_t)n * K + 32 * b + 8 * g;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    v |= (uint32_t)(src[r] & 0x0Fu) << (4 * (r / 2) + 16 * (r % 2));
+            }
         }
         out[i] = v;
     }
@@ -1261,6 +1304,7 @@ struct GemvArgs {
     float *y;
     int M, N, K, L, tps;
     Plan plan;
+    SegItems items;  // the segment form's matrices
 };
 
 template <bool BF16, int R, int D, bool SPLIT, int XL>
@@ -1354,11 +1398,11 @@ static void launch_seg_t(const GemvArgs &a)
     }();
     (void)lds_raised;
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.tps);
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.items,
+                           a.M, a.K, a.plan, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.tps);
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.items,
+                           a.M, a.K, a.plan, a.tps);
 }
 
 template <bool BF16, int R, int LQ>
@@ -1403,12 +1447,25 @@ static void launch_seg_b(int R, int LQ, const GemvArgs &a)
 // The segment-stationary form applies with S = 16 segments of at most 3
 // quads, more than 256 column tiles and its LDS within 160 KB.  tpw: tiles
 // per workgroup, about one workgroup per compute unit.
-static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
+static bool seg_fits_k(int M, const Plan &plan, int &LQ)
 {
     if (plan.S != 16)
         return false;
     LQ = (plan.G + 15) / 16;
-    if (LQ > 3 || (LQ == 3 && M > 8))  // 3-quad segments at R = 4: 128 registers do not hold them
+    // 3-quad segments at R = 4: 128 registers do not hold them
+    return !(LQ > 3 || (LQ == 3 && M > 8));
+}
+
+static size_t seg_lds_bytes(int M, int tpw)
+{
+    const int MR = M < 16 ? M : 16;
+    const int tc = seg_tc(M, tpw);
+    return (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw);
+}
+
+static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
+{
+    if (!seg_fits_k(M, plan, LQ))
         return false;
     const int tiles = (N + 15) / 16;
     // measured on MI355X: with one tile per workgroup or fewer (N <= 4096)
@@ -1419,9 +1476,7 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
     if (tiles <= 256 || (tiles <= 512 && (LQ == 3 || (LQ == 2 && M <= 4))))
         return false;
     tpw = (tiles + 255) / 256;
-    const int MR = M < 16 ? M : 16;
-    const int tc = seg_tc(M, tpw);
-    lds = (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw);
+    lds = seg_lds_bytes(M, tpw);
     return lds <= SEG_LDS_MAX;
 }
 
@@ -1451,6 +1506,13 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
             a.L = 1;
             a.tps = tpw;
             a.plan = plan;
+            a.items = SegItems{};
+            a.items.count = 1;
+            a.items.wg_end[0] = (int)a.grid.x;
+            a.items.wq[0] = wq;
+            a.items.scales[0] = scales;
+            a.items.y[0] = y;
+            a.items.N[0] = N;
             if (bf16)
                 launch_seg_b<true>(R, LQ, a);
             else
@@ -1489,6 +1551,58 @@ hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16
     else
         launch_gemv_b<false>(R, sh, a);
     return hipGetLastError();
+}
+
+bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
+                         hipStream_t stream, hipError_t *err)
+{
+    const Plan plan = make_plan(K);
+    int LQ;
+    if (count < 1 || count > kGroupMax || !seg_fits_k(M, plan, LQ))
+        return false;
+    // tiles per workgroup from the group's total, about one workgroup per
+    // compute unit over all of them; each matrix gets whole workgroups
+    long long tiles = 0;
+    for (int i = 0; i < count; ++i)
+        tiles += (items[i].N + 15) / 16;
+    const int tpw = (int)((tiles + 255) / 256);
+    const size_t lds = seg_lds_bytes(M, tpw);
+    if (lds > SEG_LDS_MAX)
+        return false;
+    GemvArgs a;
+    a.items = SegItems{};
+    a.items.count = count;
+    int wg = 0;
+    for (int i = 0; i < count; ++i) {
+        wg += ((items[i].N + 15) / 16 + tpw - 1) / tpw;
+        a.items.wg_end[i] = wg;
+        a.items.wq[i] = items[i].wq;
+        a.items.scales[i] = items[i].scales;
+        a.items.y[i] = items[i].y;
+        a.items.N[i] = items[i].N;
+    }
+    a.grid = dim3((unsigned)wg, (unsigned)((M + 15) / 16));
+    a.block = dim3(1024);
+    a.lds = lds;
+    a.stream = stream;
+    a.x = (const uint16_t *)x;
+    a.wq = nullptr;
+    a.scales = nullptr;
+    a.y = nullptr;
+    a.M = M;
+    a.N = 0;
+    a.K = K;
+    a.L = 1;
+    a.tps = tpw;
+    a.plan = plan;
+    const int rows = M < 16 ? M : 16;
+    const int R = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;
+    if (bf16)
+        launch_seg_b<true>(R, LQ, a);
+    else
+        launch_seg_b<false>(R, LQ, a);
+    *err = hipGetLastError();
+    return true;
 }
 
 static constexpr int kComputeUnits = 256;
@@ -1643,12 +1757,17 @@ size_t packed_code_bytes(int N, int K) { return (size_t)((N + 15) / 16) * ((K / 
 
 size_t packed_scale_bytes(int N, int K) { return (size_t)((N + 15) / 16) * ((K / 32 + 3) / 4) * 128; }
 
-hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales_in, uint8_t *wq, uint16_t *scales_out,
-                       int N, int K, hipStream_t stream)
+hipError_t launch_pack(const uint8_t *codes, bool nibbles, const uint16_t *scales_in, uint8_t *wq,
+                       uint16_t *scales_out, int N, int K, hipStream_t stream)
 {
     const size_t items = packed_code_bytes(N, K) / 16;
-    hipLaunchKernelGGL(q4_pack_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, codes,
-                       scales_in, wq, scales_out, N, K, items);
+    const dim3 grid((unsigned)((items + 255) / 256));
+    if (nibbles)
+        hipLaunchKernelGGL(q4_pack_kernel<true>, grid, dim3(256), 0, stream, codes, scales_in, wq, scales_out, N, K,
+                           items);
+    else
+        hipLaunchKernelGGL(q4_pack_kernel<false>, grid, dim3(256), 0, stream, codes, scales_in, wq, scales_out, N,
+                           K, items);
     return hipGetLastError();
 }
 

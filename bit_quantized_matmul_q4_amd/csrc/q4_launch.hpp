@@ -12,6 +12,20 @@ namespace q4 {
 hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
                        float *y, int M, int N, int K, hipStream_t stream);
 
+// One matrix of a group that shares x, M and K.
+struct GroupItem {
+    const uint8_t *wq;
+    const uint16_t *scales;
+    float *y;
+    int N;
+};
+
+// The group (1..8 matrices) in one launch of the matrix-vector kernel's
+// segment form.  Returns false, launching nothing, where that form does not
+// apply to K (then *err is untouched); else the launch status in *err.
+bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
+                         hipStream_t stream, hipError_t *err);
+
 // LDS-staged matrix-matrix kernel.  workspace may be NULL (no split of K
 // across workgroups); otherwise it holds workspace_bytes bytes.
 hipError_t launch_gemm(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
@@ -27,9 +41,10 @@ size_t gemm_workspace_bytes(int M, int N, int K);
 constexpr size_t kScratchBytes = size_t(4) << 20;
 hipError_t scratch_buffer(void **ptr);
 
-// Canonical codes [N][K] and scales [N][K/32] -> the tiled layout.
-hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales_in, uint8_t *wq, uint16_t *scales_out,
-                       int N, int K, hipStream_t stream);
+// Canonical codes ([N][K] one per byte, or nibble rows [N][K/2]) and
+// scales [N][K/32] -> the tiled layout.
+hipError_t launch_pack(const uint8_t *codes, bool nibbles, const uint16_t *scales_in, uint8_t *wq,
+                       uint16_t *scales_out, int N, int K, hipStream_t stream);
 
 // Dense weights [N][K] (kind 0 binary16, 1 bfloat16, 2 binary32) ->
 // canonical codes [N][K] and binary16 scales [N][K/32].

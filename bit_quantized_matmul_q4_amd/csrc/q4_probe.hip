@@ -1,4 +1,5 @@
-// q4_probe.hip -- probe kernels for the GPU tests (libq4probe.so).
+// q4_probe.hip -- probe kernels for the GPU tests and the benchmark's
+// calibration read (libq4probe.so).
 //
 // They run the library's own device primitives (q4_device.hpp) on raw lane
 // data so the tests can check, on the hardware, the assumptions the fixed
@@ -6,6 +7,11 @@
 // MFMA result element depends only on its own A row and B column (not on its
 // slot or on other rows), run-to-run determinism, the nibble dequantization
 // and the corrected block dot.  Not part of the product library.
+//
+// probe_read is a plain streaming read of a device buffer: the benchmark's
+// yardstick of the bandwidth the memory system delivers to a simple kernel
+// ("a big copy, not the spec sheet", in "Why LLM Decoding Is Slow, and Why
+// Batching Is (Almost) Free", section "First Attempt: A Faster Chip").
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,9 +60,45 @@ __global__ __launch_bounds__(256) void probe_fma0(const float *d, const float *s
         out[i] = __builtin_fmaf(d[i], s[i], 0.0f);
 }
 
+// Grid-stride 16-byte non-temporal loads, eight in flight per thread; the
+// xor of everything read goes to sink[0] only if it equals a value no real
+// buffer is known to give, so the loads cannot be dropped and nothing else
+// is written.  n16: number of 16-byte words.
+__global__ __launch_bounds__(512) void probe_read(const q4::u32x4 *__restrict__ src, size_t n16, uint32_t *sink)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    q4::u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        q4::u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc ^= v[u];
+    }
+    for (; i < n16; i += stride)
+        acc ^= __builtin_nontemporal_load(src + i);
+    const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (r == 0x9E3779B9u)
+        sink[0] = r;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Streams `bytes` (a multiple of 16, src 16-byte aligned) with `blocks`
+// workgroups of 512 threads.
+int q4probe_read(const void *src, size_t bytes, void *sink, int blocks, void *stream)
+{
+    if (!src || !sink || bytes % 16 || blocks < 1)
+        return -1;
+    hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(512), 0, (hipStream_t)stream, (const q4::u32x4 *)src,
+                       bytes / 16, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 int q4probe_mfma(const void *a, const void *b, void *d, int waves, int bf16, void *stream)
 {

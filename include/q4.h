@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 5
+#define Q4_ABI_VERSION 6
 
 enum q4_status {
     Q4_OK = 0,
@@ -142,6 +142,47 @@ size_t q4_workspace_bytes(int M, int N, int K, int kernel);
  */
 int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
             void *stream);
+
+/*
+ * q4_pack for codes given as nibble rows, the plain 4-bit row-major form:
+ *   Wq_rows  uint8 [N][K/2]   device, any alignment; byte j of row n holds
+ *                             k = 2j in bits 0..3 and k = 2j + 1 in bits 4..7
+ * Other arguments, results and errors as q4_pack (bit-exact; the same packed
+ * bytes as q4_pack of the unpacked codes).
+ */
+int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
+                    void *stream);
+
+/*
+ * Grouped launch: several weight matrices that take the same x (same M, K
+ * and activation type), e.g. a layer's q, k and v projections and its gate
+ * and up projections, in one dispatch, so the launch and ramp cost of the
+ * matrix-vector kernel is paid once for all of them (the per-call dispatch
+ * cost "Why Continuous Batching Slowed Down My LLM Inference Engine: A Metal
+ * Kernel Investigation", section "Row-by-Row GEMV to the Rescue", blames
+ * for the row-by-row scheme's slowdown).
+ *   x        [M][K] bf16 or binary16 (x_dtype), device, 16-byte aligned
+ *   items    host array of `count` (1..Q4_GROUP_MAX) matrices: packed Wq and
+ *            scales of an N_i x K weight (alignment as q4_linear) and y_i
+ *            fp32 [M][N_i] (4-byte aligned, overwritten); the y_i must not
+ *            overlap each other or any input
+ * Every y_i is bit-identical to q4_linear_ex's for that matrix (any kernel):
+ * the reduction order depends on K only.  One launch when the crossover rule
+ * picks the matrix-vector kernel and K has 16 segments of at most 3 quads
+ * (2048 <= K <= 6144; up to 8 rows when the segments hold 3 quads), else one
+ * call per matrix with the rule's kernel and no workspace.  All argument
+ * checks (every item's) run before any HIP call.  No allocation.
+ */
+#define Q4_GROUP_MAX 8
+typedef struct q4_group_item {
+    const void *Wq;
+    const void *scales;
+    float *y;
+    int N;
+} q4_group_item;
+
+int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, int count, int M, int K,
+                      void *stream);
 
 /*
  * Quantize dense weights into the canonical form (the input of q4_pack).

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_and_strerror(lib):
-    assert lib.q4_abi_version() == 5
+    assert lib.q4_abi_version() == 6
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.q4_strerror(st) and lib.q4_strerror(st) != b"unknown status"
     assert lib.q4_strerror(-99) == b"unknown status"
@@ -202,3 +202,29 @@ def test_noalloc_argument_checks(lib):
     assert lib.q4_linear_noalloc(p, 1, p, p, y, 0, 16, 32, 0, None) == -2
     assert lib.q4_linear_noalloc(p, 1, p, p, y, 1, 16, 48, 0, None) == -2
     assert lib.q4_linear_noalloc(ctypes.c_void_p(4104), 1, p, p, y, 1, 16, 32, 0, None) == -3
+
+
+def test_grouped_argument_checks(lib):
+    """q4_linear_grouped checks the group and every item before any HIP call."""
+    p = ctypes.c_void_p(4096)
+    items = (_lib.GroupItem * 9)()
+    for i in range(9):
+        items[i] = _lib.GroupItem(4096, 4096, 4096, 64)
+    assert lib.q4_linear_grouped(p, 1, items, 0, 1, 3584, None) == -2
+    assert lib.q4_linear_grouped(p, 1, items, 9, 1, 3584, None) == -2
+    assert lib.q4_linear_grouped(None, 1, items, 2, 1, 3584, None) == -1
+    assert lib.q4_linear_grouped(p, 5, items, 2, 1, 3584, None) == -4
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3000, None) == -2
+    items[1] = _lib.GroupItem(4096, None, 4096, 64)
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -1
+    items[1] = _lib.GroupItem(4096, 4096, 4096, 0)
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -2
+    items[1] = _lib.GroupItem(4104, 4096, 4096, 64)
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -3
+
+
+def test_pack_nibbles_argument_checks(lib):
+    p = ctypes.c_void_p(4096)
+    assert lib.q4_pack_nibbles(None, p, p, p, 16, 64, None) == -1
+    assert lib.q4_pack_nibbles(p, p, p, p, 16, 48, None) == -2
+    assert lib.q4_pack_nibbles(p, p, ctypes.c_void_p(4100), p, 16, 64, None) == -3
