@@ -215,10 +215,12 @@ def linear_noalloc(x: torch.Tensor, w: Q4Weight, out: torch.Tensor, kernel: str 
     return out
 
 
-def linear_grouped(x: torch.Tensor, weights, outs=None) -> list:
+def linear_grouped(x: torch.Tensor, weights, outs=None, workspace: torch.Tensor | bool | None = True) -> list:
     """q4_linear_grouped: y_i = x . dequant(w_i)^T for 1..8 weights sharing
     x's K, in one launch where the matrix-vector kernel's segment form
-    applies.  Returns the outputs (allocated unless ``outs`` is given)."""
+    applies (else one call per weight, with ``workspace`` as in ``linear``:
+    True allocates the largest one the calls can use).  Returns the outputs
+    (allocated unless ``outs`` is given)."""
     lib = _lib.load()
     _need(x, "x", (torch.bfloat16, torch.float16), 2)
     dev = x.device
@@ -246,9 +248,18 @@ def linear_grouped(x: torch.Tensor, weights, outs=None) -> list:
         if tuple(y.shape) != (M, w.N):
             raise ValueError("out %d must be [%d, %d]" % (i, M, w.N))
         items[i] = _lib.GroupItem(w.codes.data_ptr(), w.scales.data_ptr(), y.data_ptr(), w.N)
+    ws_ptr, ws_len = None, 0
+    if isinstance(workspace, torch.Tensor):
+        _need(workspace, "workspace", (torch.uint8,), 1, dev)
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel()
+    elif workspace:
+        need = max(lib.q4_workspace_bytes(M, w.N, K, _lib.Q4_AUTO) for w in weights)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws_ptr, ws_len = ws.data_ptr(), need
     dtype = _lib.Q4_BF16 if x.dtype == torch.bfloat16 else _lib.Q4_F16
     with torch.cuda.device(dev):
-        st = lib.q4_linear_grouped(x.data_ptr(), dtype, items, len(weights), M, K, _stream(dev))
+        st = lib.q4_linear_grouped(x.data_ptr(), dtype, items, len(weights), M, K, ws_ptr, ws_len, _stream(dev))
     _lib.check(st, "q4_linear_grouped")
     return outs
 

@@ -73,7 +73,7 @@ def _declare(lib):
     lib.q4_linear_ex.restype = i
     lib.q4_linear_noalloc.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     lib.q4_linear_noalloc.restype = i
-    lib.q4_linear_grouped.argtypes = [vp, i, ctypes.POINTER(GroupItem), i, i, i, vp]
+    lib.q4_linear_grouped.argtypes = [vp, i, ctypes.POINTER(GroupItem), i, i, i, vp, sz, vp]
     lib.q4_linear_grouped.restype = i
     lib.q4_pack_nibbles.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.q4_pack_nibbles.restype = i

@@ -288,10 +288,14 @@ int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, voi
 }
 
 int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, int count, int M, int K,
-                      void *stream)
+                      void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!x || !items)
         return Q4_ERR_NULL;
+    if (workspace_bytes > 0 && !workspace)
+        return Q4_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256))
+        return Q4_ERR_ALIGN;
     if (x_dtype != Q4_F16 && x_dtype != Q4_BF16)
         return Q4_ERR_ENUM;
     if (count < 1 || count > Q4_GROUP_MAX)
@@ -313,15 +317,17 @@ int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, in
     const bool bf16 = x_dtype == Q4_BF16;
     hipStream_t s = (hipStream_t)stream;
     // one launch where the crossover rule picks the matrix-vector kernel and
-    // its segment form fits K; otherwise each matrix as q4_linear would run it
+    // its segment form fits K; otherwise each matrix as q4_linear_ex (Q4_AUTO)
+    // would run it with this workspace (the calls are stream-ordered, so
+    // they can share it)
     if (auto_kernel(M, K, false) == Q4_GEMV) {
         hipError_t e = hipSuccess;
         if (q4::launch_gemv_grouped(x, bf16, g, count, M, K, s, &e))
             return hip_status(e);
     }
     for (int i = 0; i < count; ++i) {
-        const int st = linear_impl(x, x_dtype, g[i].wq, g[i].scales, g[i].y, M, g[i].N, K, Q4_AUTO, nullptr, 0,
-                                   false, stream);
+        const int st = linear_impl(x, x_dtype, g[i].wq, g[i].scales, g[i].y, M, g[i].N, K, Q4_AUTO, workspace,
+                                   workspace_bytes, false, stream);
         if (st != Q4_OK)
             return st;
     }

@@ -170,8 +170,10 @@ int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, voi
  * the reduction order depends on K only.  One launch when the crossover rule
  * picks the matrix-vector kernel and K has 16 segments of at most 3 quads
  * (2048 <= K <= 6144; up to 8 rows when the segments hold 3 quads), else one
- * call per matrix with the rule's kernel and no workspace.  All argument
- * checks (every item's) run before any HIP call.  No allocation.
+ * call per matrix as q4_linear_ex with Q4_AUTO and the given workspace
+ * (optional, as for q4_linear_ex; the calls run in stream order, so one
+ * workspace of the largest item's q4_workspace_bytes serves them all).  All
+ * argument checks (every item's) run before any HIP call.  No allocation.
  */
 #define Q4_GROUP_MAX 8
 typedef struct q4_group_item {
@@ -182,7 +184,7 @@ typedef struct q4_group_item {
 } q4_group_item;
 
 int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, int count, int M, int K,
-                      void *stream);
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Quantize dense weights into the canonical form (the input of q4_pack).

@@ -210,17 +210,20 @@ def test_grouped_argument_checks(lib):
     items = (_lib.GroupItem * 9)()
     for i in range(9):
         items[i] = _lib.GroupItem(4096, 4096, 4096, 64)
-    assert lib.q4_linear_grouped(p, 1, items, 0, 1, 3584, None) == -2
-    assert lib.q4_linear_grouped(p, 1, items, 9, 1, 3584, None) == -2
-    assert lib.q4_linear_grouped(None, 1, items, 2, 1, 3584, None) == -1
-    assert lib.q4_linear_grouped(p, 5, items, 2, 1, 3584, None) == -4
-    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3000, None) == -2
+    assert lib.q4_linear_grouped(p, 1, items, 0, 1, 3584, None, 0, None) == -2
+    assert lib.q4_linear_grouped(p, 1, items, 9, 1, 3584, None, 0, None) == -2
+    assert lib.q4_linear_grouped(None, 1, items, 2, 1, 3584, None, 0, None) == -1
+    assert lib.q4_linear_grouped(p, 5, items, 2, 1, 3584, None, 0, None) == -4
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3000, None, 0, None) == -2
     items[1] = _lib.GroupItem(4096, None, 4096, 64)
-    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -1
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None, 0, None) == -1
     items[1] = _lib.GroupItem(4096, 4096, 4096, 0)
-    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -2
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None, 0, None) == -2
     items[1] = _lib.GroupItem(4104, 4096, 4096, 64)
-    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None) == -3
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None, 0, None) == -3
+    items[1] = _lib.GroupItem(4096, 4096, 4096, 64)
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, None, 64, None) == -6
+    assert lib.q4_linear_grouped(p, 1, items, 2, 1, 3584, ctypes.c_void_p(4160), 64, None) == -3
 
 
 def test_pack_nibbles_argument_checks(lib):
