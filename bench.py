@@ -236,7 +236,7 @@ def main() -> int:
     plib.q4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     plib.q4probe_read.restype = ctypes.c_int
     calib = None
-    if not args.headline_only:
+    if not (args.headline_only or args.eager_step):
         cbuf = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         sink = torch.zeros(4, dtype=torch.int32, device=dev)
         best = (1e30, 0)
