@@ -110,6 +110,31 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
     }
 }
 
+// gemv_quad with the quad's correction dots already computed (Eq[i][r]: the
+// value E of block i for accumulator row r), for waves that hold their x
+// for many tiles: E depends on x only, so the same instruction on the same
+// operands gives the same bits wherever it runs.
+template <bool BF16, int R, bool SHORT>
+__device__ __forceinline__ void gemv_quad_pre(const GemvStage &st, const u32x4 (&xa)[4], const float (&Eq)[4][R],
+                                              int nq, const Dequant<BF16> &dq, float (&p)[R])
+{
+    const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+    const uint32_t h[4] = {st.s.x & 0xFFFFu, st.s.x >> 16, st.s.y & 0xFFFFu, st.s.y >> 16};
+    f32x4 D[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        D[i] = blockdot<BF16>(xa[i], dq(w[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!SHORT || i < nq) {
+            const float d = half_bits_to_float(h[i]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                p[r] = __builtin_fmaf(d, block_value<BF16>(D[i][r], Eq[i][r]), p[r]);
+        }
+    }
+}
+
 // The wave's stream is a contiguous run of tile-quads: quad i of the stream
 // sits at code byte 1024 i and scale byte 128 i from the wave's base, and is
 // quad q0 + (i mod RQ) of K.  The code and scale resources span exactly the
@@ -653,6 +678,21 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): x and the prefill (see q4_gemv)
 
     const Dequant<BF16> dq;
+    // bf16: the segment's correction dots once, for all the wave's tiles,
+    // where the registers allow (LQ 4 R values a lane)
+    constexpr bool HOIST = kCorrected<BF16> && LQ * 4 * R <= 16;
+    float Eh[LQ][4][R];
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int q = 0; q < LQ; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x4 e = blockdot<BF16>(xs[q][b], dq.offset);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    Eh[q][b][r] = e[r];
+            }
+    }
     float p[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -663,7 +703,10 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         const int i = pos / LQ;
         if (q < len) {
             const int nq = SHORT && qs + q == G - 1 ? plan.nb - 4 * (G - 1) : 4;
-            gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
+            if constexpr (HOIST)
+                gemv_quad_pre<BF16, R, SHORT>(ring[d], xs[q], Eh[q], nq, dq, p);
+            else
+                gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
         }
         if (q == LQ - 1) {  // the tile's segment partial is done
             float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
