@@ -89,11 +89,16 @@ enum q4_kernel {
  *   scales packed scales         device, 8-byte aligned, q4_packed_scale_bytes(N, K)
  *   y      fp32  [M][N]          device, 4-byte aligned, overwritten
  * Kernel chosen by the crossover rule (Q4_AUTO), with no workspace.
+ * Source: "Why Continuous Batching Slowed Down My LLM Inference Engine: A
+ * Metal Kernel Investigation", section "Two Rows of Input, Two Different
+ * Kernels" (one quantized weight matrix applied to the batch's rows); the
+ * signature and weight format are the task spec's.
  */
 int q4_linear(const void *x, const void *Wq, const void *scales, float *y,
               int M, int N, int K, void *stream);
 
-/* Same as q4_linear with binary16 activations. */
+/* Same as q4_linear with binary16 activations (the fp16 workloads: the
+ * single matvec and the Qwen2.5-0.5B-shaped set; task spec). */
 int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y,
                   int M, int N, int K, void *stream);
 
@@ -105,6 +110,10 @@ int q4_linear_f16(const void *x, const void *Wq, const void *scales, float *y,
  * q4_workspace_bytes() gives the size that enables the full split for a
  * shape.  A workspace smaller than that is used for a smaller split.
  * Two calls that share one workspace must not overlap in time.
+ * Source: the same page, sections "Two Rows of Input, Two Different Kernels"
+ * (matrix-vector vs matrix-matrix kernel) and "Row-by-Row GEMV to the
+ * Rescue" (forcing the matrix-vector kernel); the bits do not depend on the
+ * kernel (section "Same Prompt, Different Story").
  */
 int q4_linear_ex(const void *x, int x_dtype, const void *Wq, const void *scales,
                  float *y, int M, int N, int K, int kernel,
@@ -129,7 +138,8 @@ int q4_linear_noalloc(const void *x, int x_dtype, const void *Wq, const void *sc
                       float *y, int M, int N, int K, int kernel, void *stream);
 
 /* Workspace bytes that q4_linear_ex can use for this shape and kernel
- * (0 if the kernel uses none).  Pure host computation; 0 for bad shapes. */
+ * (0 if the kernel uses none).  Pure host computation; 0 for bad shapes.
+ * (Library detail; the pages are silent.) */
 size_t q4_workspace_bytes(int M, int N, int K, int kernel);
 
 /*
@@ -139,6 +149,8 @@ size_t q4_workspace_bytes(int M, int N, int K, int kernel);
  *   Wq       packed codes     device, 16-byte aligned, q4_packed_code_bytes(N, K)
  *   Wscales  packed scales    device, 8-byte aligned, q4_packed_scale_bytes(N, K)
  * K must be a positive multiple of 32.  Bit-exact; padding is written as 0.
+ * Source: task spec (the pages say only "4-bit quantized": "Why Continuous
+ * Batching Slowed Down My LLM Inference Engine", introduction).
  */
 int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
             void *stream);
@@ -149,6 +161,7 @@ int q4_pack(const uint8_t *codes, const void *scales, uint8_t *Wq, void *Wscales
  *                             k = 2j in bits 0..3 and k = 2j + 1 in bits 4..7
  * Other arguments, results and errors as q4_pack (bit-exact; the same packed
  * bytes as q4_pack of the unpacked codes).
+ * Source: task spec (its packed Wq [N x K/2] input format).
  */
 int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, void *Wscales, int N, int K,
                     void *stream);
@@ -195,6 +208,8 @@ int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, in
  *     q = clamp(round_half_even(w / d), -8, 7) + 8, on the exact quotient;
  *     a block whose d rounds to zero gets d = +0 and every code 8.
  * Both roundings are exact, so the result is bit-reproducible anywhere.
+ * Source: none on the pages (they never say how the 4-bit codes are made);
+ * the plain absmax rule is this library's reading.
  *   w        [N][K] row-major, w_dtype Q4_F32, Q4_BF16 or Q4_F16; device,
  *            16-byte aligned.  Values must be finite with absmax / 7 below
  *            65520 (the binary16 overflow threshold); a block outside that
@@ -207,7 +222,7 @@ int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, in
 int q4_quantize(const void *w, int w_dtype, uint8_t *codes, void *scales, int N, int K, void *stream);
 
 /* Bytes of the packed codes and packed scales of an N x K matrix (0 for a
- * bad shape).  Pure host computation. */
+ * bad shape).  Pure host computation.  (Library layout; pages silent.) */
 size_t q4_packed_code_bytes(int N, int K);
 size_t q4_packed_scale_bytes(int N, int K);
 
@@ -217,21 +232,26 @@ size_t q4_packed_scale_bytes(int N, int K);
  * Q4_AUTO) asks for (q4_linear, which has none, then keeps the matrix-vector
  * kernel).  T is initialised from the environment variable Q4_CROSSOVER if
  * set, else the measured default.  q4_set_crossover returns Q4_ERR_SHAPE for
- * T < 0.  The rule never changes results, only speed. */
+ * T < 0.  The rule never changes results, only speed.
+ * Source: "Why Continuous Batching Slowed Down My LLM Inference Engine",
+ * sections "Two Rows of Input, Two Different Kernels" (switch at one row)
+ * and "Row-by-Row GEMV to the Rescue" (a measured threshold of 4). */
 int q4_get_crossover(void);
 int q4_set_crossover(int T);
 
 /* Number of K-segments the fixed reduction order uses for this K (1..16),
- * or 0 if K is not a positive multiple of 32.  It depends on K only. */
+ * or 0 if K is not a positive multiple of 32.  It depends on K only (the
+ * fixed order answers that page's section "Same Prompt, Different Story"). */
 int q4_segments(int K);
 
-/* Human-readable text for a status code (static storage). */
+/* Human-readable text for a status code (static storage).  (Library.) */
 const char *q4_strerror(int status);
 
-/* HIP error code of the last Q4_ERR_HIP on the calling thread (0 if none). */
+/* HIP error code of the last Q4_ERR_HIP on the calling thread (0 if none).
+ * (Library.) */
 int q4_last_hip_error(void);
 
-/* Q4_ABI_VERSION of the loaded library. */
+/* Q4_ABI_VERSION of the loaded library.  (Library.) */
 int q4_abi_version(void);
 
 #ifdef __cplusplus
