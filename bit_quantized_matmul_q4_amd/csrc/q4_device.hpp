@@ -58,14 +58,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------- dequant
 // bf16: the 16-bit pattern 0x4180 | (q << 3), q in 0..15, is 16 + q exactly
 // (16 = 0x4180, the code in the top four of the seven mantissa bits).
-// fp16: 0x6400 | q is 1024 + q exactly (the ulp on [1024, 2048) is 1), and
-// one packed fp16 add of -1032 (exact: the result is an integer in -8..7)
-// leaves q - 8.
+// fp16: 0x6400 | q is 1024 + q exactly (the ulp on [1024, 2048) is 1) and
+// 0x6400 | (q << 4) is 1024 + 16 q; one packed fp16 add of -1032, or one
+// packed fma by 1/16 with -72, leaves q - 8 (exact: the result is an integer
+// in -8..7).  So the codes at bits 4..7 of each half need no shift.
 template <bool BF16>
 constexpr uint32_t kMask = BF16 ? 0x00780078u : 0x000F000Fu;
 template <bool BF16>
 constexpr uint32_t kMagic = BF16 ? 0x41804180u : 0x64006400u;
-constexpr uint32_t kF16Bias = 0xE408E408u;  // -1032, -1032 (binary16)
+constexpr uint32_t kF16MaskHi = 0x00F000F0u;   // codes at bits 4..7 of each half
+constexpr uint32_t kF16Bias = 0xE408E408u;     // -1032, -1032 (binary16)
+constexpr uint32_t kF16Sixteenth = 0x2C002C00u;  // 1/16, 1/16
+constexpr uint32_t kF16Bias16 = 0xD480D480u;   // -72, -72
 // B operand of the bf16 correction dot E: 24 in every entry.
 constexpr uint32_t kBf16Offset = 0x41C041C0u;
 // Whether the block dot carries the correction E (bf16) or is exact (fp16).
@@ -74,58 +78,70 @@ constexpr bool kCorrected = BF16;
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// One packed word (code r at bit 4 (r / 2) + 16 (r % 2)) -> the eight
-// operand values in natural k order, two per dword.  bf16: the pair's codes
-// moved to bits 3..6 of each half (pair 0 up by 3, pairs 1..3 down by 1, 5,
-// 9), masked and or-ed with the magic.  fp16: masked in place and or-ed,
-// then the packed add.  mask, magic and bias must arrive as opaque registers
-// (see Dequant): as literals the compiler splits each step in two (this
-// target's three-operand instructions take no literal).
-template <bool BF16>
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, uint32_t mask, uint32_t magic, uint32_t bias)
-{
-    u32x4 r;
-    if constexpr (BF16) {
-        r.x = ((w << 3) & mask) | magic;
-        r.y = ((w >> 1) & mask) | magic;
-        r.z = ((w >> 5) & mask) | magic;
-        r.w = ((w >> 9) & mask) | magic;
-    } else {
-        const f16x2 b = __builtin_bit_cast(f16x2, bias);
-        r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w & mask) | magic) + b);
-        r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 4) & mask) | magic) + b);
-        r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 8) & mask) | magic) + b);
-        r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 12) & mask) | magic) + b);
-    }
-    return r;
-}
-
-// The dequant constants in registers the compiler cannot fold: the mask and
-// the fp16 bias in scalar registers, the magic in a vector one (one scalar
-// operand per instruction on this target).  The empty statements emit no
-// instructions.  The bf16 correction's B operand (24 everywhere) is built
-// once the same way, so the compiler keeps it in four registers instead of
-// rebuilding it for every block dot.
+// The dequant constants in registers the compiler cannot fold: the masks and
+// the fp16 biases in scalar registers, the magic and 1/16 in vector ones (one
+// scalar operand per instruction on this target; three-operand instructions
+// take no literal).  The empty statements emit no instructions.  The bf16
+// correction's B operand (24 everywhere) is built once the same way, so the
+// compiler keeps it in four registers instead of rebuilding it for every
+// block dot.
 template <bool BF16>
 struct Dequant {
-    uint32_t mask, magic, bias;
+    uint32_t mask, magic, mask_hi, bias, bias16, sixteenth;
     u32x4 offset;
     __device__ __forceinline__ Dequant()
     {
         mask = kMask<BF16>;
         magic = kMagic<BF16>;
-        bias = kF16Bias;
         asm volatile("" : "+s"(mask));
         asm volatile("" : "+v"(magic));
         if constexpr (BF16) {
+            mask_hi = bias = bias16 = sixteenth = 0u;
             offset = (u32x4){kBf16Offset, kBf16Offset, kBf16Offset, kBf16Offset};
             asm volatile("" : "+v"(offset));
         } else {
+            mask_hi = kF16MaskHi;
+            bias = kF16Bias;
+            bias16 = kF16Bias16;
+            sixteenth = kF16Sixteenth;
             offset = (u32x4){0u, 0u, 0u, 0u};
+            asm volatile("" : "+s"(mask_hi));
             asm volatile("" : "+s"(bias));
+            asm volatile("" : "+s"(bias16));
+            asm volatile("" : "+v"(sixteenth));
         }
     }
-    __device__ __forceinline__ u32x4 operator()(uint32_t w) const { return dequant8<BF16>(w, mask, magic, bias); }
+
+    // One packed word (code r at bit 4 (r / 2) + 16 (r % 2)) -> the eight
+    // operand values in natural k order, two per dword.  bf16: each pair's
+    // codes moved to bits 3..6 of each half (pair 0 up by 3, pairs 1..3 down
+    // by 1, 5, 9), masked and or-ed with the magic: 8 operations.  fp16:
+    // pairs 0 and 1 masked in place, pairs 2 and 3 from one shift by 8, then
+    // the packed add (pairs 0, 2) or fma (pairs 1, 3): 9 operations.
+    __device__ __forceinline__ u32x4 operator()(uint32_t w) const
+    {
+        u32x4 r;
+        if constexpr (BF16) {
+            r.x = ((w << 3) & mask) | magic;
+            r.y = ((w >> 1) & mask) | magic;
+            r.z = ((w >> 5) & mask) | magic;
+            r.w = ((w >> 9) & mask) | magic;
+        } else {
+            const f16x2 b = __builtin_bit_cast(f16x2, bias);
+            const f16x2 b16 = __builtin_bit_cast(f16x2, bias16);
+            const f16x2 s16 = __builtin_bit_cast(f16x2, sixteenth);
+            const uint32_t w8 = w >> 8;
+            const f16x2 v0 = __builtin_bit_cast(f16x2, (w & mask) | magic);
+            const f16x2 v1 = __builtin_bit_cast(f16x2, (w & mask_hi) | magic);
+            const f16x2 v2 = __builtin_bit_cast(f16x2, (w8 & mask) | magic);
+            const f16x2 v3 = __builtin_bit_cast(f16x2, (w8 & mask_hi) | magic);
+            r.x = __builtin_bit_cast(uint32_t, v0 + b);
+            r.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v1, s16, b16));
+            r.z = __builtin_bit_cast(uint32_t, v2 + b);
+            r.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v3, s16, b16));
+        }
+        return r;
+    }
 };
 
 // ---------------------------------------------------------------- BlockDot
