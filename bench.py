@@ -557,10 +557,15 @@ def main() -> int:
     # microsecond of weight traffic at 8 TB/s): report us per call.
     small = {}
     wls = ([] if args.no_small else [1, 2]) + ([] if args.no_gpt2 else [6])
+    # grouped form of the sets (q4_linear_grouped): the 0.5B layer's q, k, v,
+    # gate and up in one launch (sharing x, as the 7B grouped step) and down
+    # alone; GPT-2's q, k and v in one launch and o alone
+    groups = {2: ([0, 1, 2, 3, 4], [5]), 6: ([0, 1, 2], [3])}
     for wl in wls:
         spec = synth.WORKLOADS[wl]
         smats = spec["matrices"]
         bf16 = spec["x"] == "bf16"
+        gsel = groups.get(wl)
         sbytes = sum(sum(q4.packed_sizes(m.N, m.K)) for m in smats)
         SP = int(min(2048, max(2, np.ceil(args.pool_gib * (1 << 30) / 2 / sbytes))))
         sbase, shost = [], []
@@ -588,8 +593,32 @@ def main() -> int:
             for mi, m in enumerate(smats):
                 records.sample(idx, q4.linear(sx[m.K][:M], sbase[mi]), sxh[m.K], bf16, shost[mi][0], shost[mi][1],
                                m.N, m.K, rng, n=64)
+            if gsel is not None:
+                gi, rest = gsel
+                Kg = smats[gi[0]].K
+
+                def call_set_grouped(p, M=M, ysm=ysm):
+                    q4.linear_grouped(sx[Kg][:M], [spool[p][i] for i in gi], outs=[ysm[i] for i in gi],
+                                      workspace=False)
+                    for r in rest:
+                        q4.linear(sx[smats[r].K][:M], spool[p][r], out=ysm[r])
+
+                gus = best_per_call(lambda: [call_set_grouped(p) for p in range(SP)], SP)
+                ybase = [q4.linear(sx[m.K][:M], sbase[mi]).cpu().numpy().view(np.uint32) for mi, m in enumerate(smats)]
+                yg = q4.linear_grouped(sx[Kg][:M], [sbase[i] for i in gi], workspace=False)
+                same = all(np.array_equal(yg[j].cpu().numpy().view(np.uint32), ybase[i]) for j, i in enumerate(gi))
+                gnb = nb - (len(gi) - 1) * 2 * M * Kg  # x read once for the group
+                rec[str(M)].update({"grouped_us_per_set": round(gus, 2), "grouped_calls": 1 + len(rest),
+                                    "grouped_gbs": round(gnb / (gus * 1e-6) / 1e9, 1),
+                                    "grouped_bits_identical": same})
+                records.add(spec["name"] + "_grouped", "%s in one launch + %d" % (
+                    "|".join(smats[i].name for i in gi), len(rest)), M, "auto", gus, gnb,
+                    sum(2 * M * m.N * m.K for m in smats), x=spec["x"], calls=1 + len(rest), bits_invariant=same)
         small[spec["name"]] = {"matrices": ["%s %dx%d" % (m.name, m.N, m.K) for m in smats],
-                               "x": spec["x"], "weight_copies": SP, "per_M": rec}
+                               "x": spec["x"], "weight_copies": SP, "per_M": rec,
+                               "grouped": None if gsel is None else {
+                                   "group": [smats[i].name for i in gsel[0]],
+                                   "separate": [smats[i].name for i in gsel[1]]}}
         log("%s: %s" % (spec["name"], rec))
         del spool, sbase, sx
         torch.cuda.empty_cache()

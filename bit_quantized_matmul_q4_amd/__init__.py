@@ -217,8 +217,8 @@ def linear_noalloc(x: torch.Tensor, w: Q4Weight, out: torch.Tensor, kernel: str 
 
 def linear_grouped(x: torch.Tensor, weights, outs=None, workspace: torch.Tensor | bool | None = True) -> list:
     """q4_linear_grouped: y_i = x . dequant(w_i)^T for 1..8 weights sharing
-    x's K, in one launch where the matrix-vector kernel's segment form
-    applies (else one call per weight, with ``workspace`` as in ``linear``:
+    x's K, in one launch of the matrix-vector kernel where the crossover rule
+    picks it (else one call per weight, with ``workspace`` as in ``linear``:
     True allocates the largest one the calls can use).  Returns the outputs
     (allocated unless ``outs`` is given)."""
     lib = _lib.load()

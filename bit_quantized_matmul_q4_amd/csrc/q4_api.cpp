@@ -316,11 +316,15 @@ int q4_linear_grouped(const void *x, int x_dtype, const q4_group_item *items, in
     }
     const bool bf16 = x_dtype == Q4_BF16;
     hipStream_t s = (hipStream_t)stream;
-    // one launch where the crossover rule picks the matrix-vector kernel and
-    // its segment form fits K; otherwise each matrix as q4_linear_ex (Q4_AUTO)
-    // would run it with this workspace (the calls are stream-ordered, so
-    // they can share it)
-    if (auto_kernel(M, K, false) == Q4_GEMV) {
+    // one launch of the matrix-vector kernel where the crossover rule picks
+    // it for every matrix (as q4_linear_ex with Q4_AUTO and this workspace
+    // would); otherwise, and for groups too wide for one launch, each matrix
+    // as q4_linear_ex (the calls are stream-ordered, so they can share the
+    // workspace)
+    bool ws_ok = workspace != nullptr;
+    for (int i = 0; i < count; ++i)
+        ws_ok = ws_ok && q4::gemm_workspace_bytes(M, g[i].N, K) <= workspace_bytes;
+    if (auto_kernel(M, K, ws_ok) == Q4_GEMV) {
         hipError_t e = hipSuccess;
         if (q4::launch_gemv_grouped(x, bf16, g, count, M, K, s, &e))
             return hip_status(e);

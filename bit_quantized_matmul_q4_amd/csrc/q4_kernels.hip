@@ -278,7 +278,56 @@ __device__ __forceinline__ int slot_row(int s) { return 4 * (s & 3) + (s >> 2); 
 // in different banks.
 __host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t)K * 2u + 16u; }
 
-// grid = (streams / 4 or column tiles, ceil(M / 16)).
+// The matrices one launch of a matrix-vector kernel runs (one, or a group
+// that shares x, M and K): passed by value in the kernel arguments.
+// NM: the table's size, 1 for a single matrix (a larger argument block
+// measurably slows every launch) or kGroupMax.
+constexpr int kGroupMax = 8;
+template <int NM>
+struct MatrixItems {
+    int count;
+    int wg_end[NM];  // workgroups (grid x) of matrices 0..i, cumulative
+    const uint8_t *wq[NM];
+    const uint16_t *scales[NM];
+    float *y[NM];
+    int N[NM];
+};
+
+// The workgroup's matrix (workgroups wg_end[i - 1] .. wg_end[i] - 1 run
+// matrix i) and the first workgroup of that matrix, chosen by selects on
+// uniform values: an indexed read of the argument block could be copied to
+// scratch memory.
+struct MatrixSel {
+    const uint8_t *wq;
+    const uint16_t *scales;
+    float *y;
+    int N, wg0;
+};
+template <int NM>
+__device__ __forceinline__ MatrixSel select_matrix(const MatrixItems<NM> items)
+{
+    int it = 0;
+#pragma unroll
+    for (int i = 1; i < NM; ++i)
+        if (i < items.count && (int)blockIdx.x >= items.wg_end[i - 1])
+            it = i;
+    MatrixSel m{items.wq[0], items.scales[0], items.y[0], items.N[0], 0};
+#pragma unroll
+    for (int i = 1; i < NM; ++i)
+        if (i == it) {
+            m.wq = items.wq[i];
+            m.scales = items.scales[i];
+            m.y = items.y[i];
+            m.N = items.N[i];
+            m.wg0 = items.wg_end[i - 1];
+        }
+    return m;
+}
+
+// grid = (streams / 4, or column tiles summed over the matrices of `items`,
+// ceil(M / 16)); SPLIT: a workgroup's matrix is the one whose range of
+// workgroup ids holds it, and its tiles count from that range's start; the
+// streaming form runs items' first matrix only.
 //  SPLIT = false: block = 256; each wave streams `tps` consecutive column
 //    tiles over all of K (one run of S segments) and stores each tile's
 //    outputs itself.
@@ -290,13 +339,18 @@ __host__ __device__ constexpr uint32_t gemv_xrow_bytes(int K) { return (uint32_t
 // Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
 // (XM_LDS) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of
 // slack, or (XM_WAVE) one slot of 4 R rows of XW_ROW bytes per wave.
-template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM>
-__global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x,
-                                                              const uint8_t *__restrict__ wq,
-                                                              const uint16_t *__restrict__ scales,
-                                                              float *__restrict__ y, int M, int N, int K,
-                                                              Plan plan, int L, int tps)
+template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM>
+__global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x, MatrixItems<NM> items,
+                                                              int M, int K, Plan plan, int L, int tps)
 {
+    // (the streaming form runs one matrix)
+    const MatrixSel sel =
+        SPLIT ? select_matrix(items) : MatrixSel{items.wq[0], items.scales[0], items.y[0], items.N[0], 0};
+    const uint8_t *__restrict__ wq = sel.wq;
+    const uint16_t *__restrict__ scales = sel.scales;
+    float *__restrict__ y = sel.y;
+    const int N = sel.N;
+    const int wgx = (int)blockIdx.x - sel.wg0;  // the workgroup within its matrix
     constexpr bool XL = XM == XM_LDS;
     // SPLIT: the run roots, [wave][row slot][column slot (17)].  Otherwise the
     // stream's tile roots (dynamic LDS): a store inside the streaming loop
@@ -321,11 +375,11 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     int t0, ntiles, run;
     if constexpr (SPLIT) {
         const int TW = (blockDim.x >> 6) >> log2W;
-        t0 = blockIdx.x * TW + (wave >> log2W);
+        t0 = wgx * TW + (wave >> log2W);
         ntiles = t0 < n16 ? 1 : 0;  // 0: a spare slot of the last workgroup
         run = wave & ((1 << log2W) - 1);
     } else {
-        t0 = (blockIdx.x * 4 + wave) * tps;
+        t0 = (wgx * 4 + wave) * tps;
         ntiles = max(0, min(tps, n16 - t0));  // 0: a spare wave of the last workgroup
         run = 0;
         if (!XL && ntiles == 0)
@@ -522,7 +576,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         __syncthreads();
         for (int o = threadIdx.x; o < TW * 256; o += blockDim.x) {
             const int slot = o >> 8, row = (o >> 4) & 15, col = o & 15;
-            const int n = 16 * (blockIdx.x * TW + slot) + col;
+            const int n = 16 * (wgx * TW + slot) + col;
             if (row < mrows && n < N) {
                 float v[8];
 #pragma unroll
@@ -551,7 +605,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // resources' ranges (zero, no memory access) and they compute nothing.
 // grid = (sum over the matrices of ceil(tiles / tpw), ceil(M / 16)),
 // block = 1024; a workgroup's matrix is the one whose range of workgroup
-// ids holds it (see SegItems).  With MR =
+// ids holds it (see MatrixItems).  With MR =
 // min(M, 16), dynamic LDS: roots [NB][TC][16 seg][MR][16] floats (NB = 1
 // if tpw <= TC: one combine after the last tile; else 2, double-buffered),
 // then outputs [tpw][MR][16] floats.
@@ -581,20 +635,9 @@ __device__ __forceinline__ void workgroup_barrier_lds()
     asm volatile("" ::: "memory");
 }
 
-// The matrices one launch of the segment form runs (one, or a group that
-// shares x, M and K): passed by value in the kernel arguments.
-constexpr int kGroupMax = 8;
-struct SegItems {
-    int count;
-    int wg_end[kGroupMax];  // workgroups (grid x) of matrices 0..i, cumulative
-    const uint8_t *wq[kGroupMax];
-    const uint16_t *scales[kGroupMax];
-    float *y[kGroupMax];
-    int N[kGroupMax];
-};
 
-template <bool BF16, int R, int LQ, bool SHORT, int TC>
-__global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x, SegItems items, int M, int K,
+template <bool BF16, int R, int LQ, bool SHORT, int TC, int NM>
+__global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x, MatrixItems<NM> items, int M, int K,
                                                     Plan plan, int tpw)
 {
     constexpr int D = seg_depth<R, LQ>();  // ring depth: a multiple of LQ
@@ -604,27 +647,11 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     float *roots = seg_lds;                                         // [NB][TC][16 seg][MR][16]
     float *ystage = seg_lds + seg_nbuf(TC, tpw) * TC * 16 * MR * 16;  // [tpw][MR][16]
 
-    // the workgroup's matrix (workgroups wg_end[i - 1] .. wg_end[i] - 1 run
-    // matrix i), chosen by selects on uniform values: an indexed read of the
-    // argument block could be copied to scratch memory
-    int it = 0;
-#pragma unroll
-    for (int i = 1; i < kGroupMax; ++i)
-        if (i < items.count && (int)blockIdx.x >= items.wg_end[i - 1])
-            it = i;
-    const uint8_t *__restrict__ wq = items.wq[0];
-    const uint16_t *__restrict__ scales = items.scales[0];
-    float *__restrict__ y = items.y[0];
-    int N = items.N[0], wg0 = 0;
-#pragma unroll
-    for (int i = 1; i < kGroupMax; ++i)
-        if (i == it) {
-            wq = items.wq[i];
-            scales = items.scales[i];
-            y = items.y[i];
-            N = items.N[i];
-            wg0 = items.wg_end[i - 1];
-        }
+    const MatrixSel sel = select_matrix(items);
+    const uint8_t *__restrict__ wq = sel.wq;
+    const uint16_t *__restrict__ scales = sel.scales;
+    float *__restrict__ y = sel.y;
+    const int N = sel.N, wg0 = sel.wg0;
 
     const int lane = threadIdx.x & 63;
     const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // segment
@@ -1342,34 +1369,80 @@ struct GemvArgs {
     size_t lds;
     hipStream_t stream;
     const uint16_t *x;
-    const uint8_t *wq;
-    const uint16_t *scales;
-    float *y;
-    int M, N, K, L, tps;
+    int M, K, L, tps;
     Plan plan;
-    SegItems items;  // the segment form's matrices
+    MatrixItems<kGroupMax> items;  // the matrices and their workgroup ranges
 };
 
-template <bool BF16, int R, int D, bool SPLIT, int XL>
-static void launch_gemv_v(const GemvArgs &a)
+// The kernels' item block for `count` matrices, matrix i taking the
+// workgroups of ceil(tiles_i / per_wg) (grid x = the return value).
+static int fill_items(MatrixItems<kGroupMax> &mi, const GroupItem *items, int count, int per_wg)
+{
+    mi = MatrixItems<kGroupMax>{};
+    mi.count = count;
+    int wg = 0;
+    for (int i = 0; i < count; ++i) {
+        wg += ((items[i].N + 15) / 16 + per_wg - 1) / per_wg;
+        mi.wg_end[i] = wg;
+        mi.wq[i] = items[i].wq;
+        mi.scales[i] = items[i].scales;
+        mi.y[i] = items[i].y;
+        mi.N[i] = items[i].N;
+    }
+    return wg;
+}
+
+// The first NM entries of the launch's table.
+template <int NM>
+static MatrixItems<NM> narrow_items(const MatrixItems<kGroupMax> &m)
+{
+    MatrixItems<NM> r{};
+    r.count = m.count;
+    for (int i = 0; i < NM; ++i) {
+        r.wg_end[i] = m.wg_end[i];
+        r.wq[i] = m.wq[i];
+        r.scales[i] = m.scales[i];
+        r.y[i] = m.y[i];
+        r.N[i] = m.N[i];
+    }
+    return r;
+}
+
+template <bool BF16, int R, int D, bool SPLIT, int XL, int NM>
+static void launch_gemv_n(const GemvArgs &a)
 {
     if constexpr (XL == XM_LDS) {
         static const bool lds_raised = [] {
             // a failure here leaves the default limit; the launch then reports it
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL, NM>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL, NM>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
             return true;
         }();
         (void)lds_raised;
     }
+    const MatrixItems<NM> items = narrow_items<NM>(a.items);
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
+                           a.M, a.K, a.plan, a.L, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL>), a.grid, a.block, a.lds, a.stream, a.x, a.wq,
-                           a.scales, a.y, a.M, a.N, a.K, a.plan, a.L, a.tps);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
+                           a.M, a.K, a.plan, a.L, a.tps);
+}
+
+// A group's table only for the split form (the streaming form runs one
+// matrix).
+template <bool BF16, int R, int D, bool SPLIT, int XL>
+static void launch_gemv_v(const GemvArgs &a)
+{
+    if constexpr (SPLIT) {
+        if (a.items.count > 1) {
+            launch_gemv_n<BF16, R, D, SPLIT, XL, kGroupMax>(a);
+            return;
+        }
+    }
+    launch_gemv_n<BF16, R, D, SPLIT, XL, 1>(a);
 }
 
 // Built variants: x in LDS with a 4-deep ring; x through per-wave slots
@@ -1428,24 +1501,34 @@ static void launch_gemv_b(int R, const GemvShape &sh, const GemvArgs &a)
 // unit, so it may take LDS beyond the default 64 KB dynamic limit.
 constexpr size_t SEG_LDS_MAX = 160 * 1024;
 
-template <bool BF16, int R, int LQ, int TC>
-static void launch_seg_t(const GemvArgs &a)
+template <bool BF16, int R, int LQ, int TC, int NM>
+static void launch_seg_n(const GemvArgs &a)
 {
     static const bool lds_raised = [] {
         // a failure here leaves the default limit; the launch then reports it
-        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, true, TC>,
+        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, true, TC, NM>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEG_LDS_MAX);
-        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, false, TC>,
+        (void)hipFuncSetAttribute((const void *)q4_gemv_seg<BF16, R, LQ, false, TC, NM>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEG_LDS_MAX);
         return true;
     }();
     (void)lds_raised;
+    const MatrixItems<NM> items = narrow_items<NM>(a.items);
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.items,
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, true, TC, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
                            a.M, a.K, a.plan, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false, TC>), a.grid, a.block, a.lds, a.stream, a.x, a.items,
+        hipLaunchKernelGGL((q4_gemv_seg<BF16, R, LQ, false, TC, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
                            a.M, a.K, a.plan, a.tps);
+}
+
+template <bool BF16, int R, int LQ, int TC>
+static void launch_seg_t(const GemvArgs &a)
+{
+    if (a.items.count > 1)
+        launch_seg_n<BF16, R, LQ, TC, kGroupMax>(a);
+    else
+        launch_seg_n<BF16, R, LQ, TC, 1>(a);
 }
 
 template <bool BF16, int R, int LQ>
@@ -1523,117 +1606,56 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
     return lds <= SEG_LDS_MAX;
 }
 
-hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
-                       float *y, int M, int N, int K, hipStream_t stream)
+// The split or streaming form over the matrices of `items` (all with the
+// shape sh); false if sh is the streaming form and there are several.
+static bool launch_gemv_items(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
+                              const Plan &plan, const GemvShape &sh, hipStream_t stream)
 {
-    const Plan plan = make_plan(K);
-    // accumulator rows per lane: ceil(rows / 4), with 3 rounded up to 4
-    const int rows = M < 16 ? M : 16;
-    const int R = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;
-    {
-        int LQ, tpw;
-        size_t lds;
-        if (seg_shape(M, N, plan, LQ, tpw, lds)) {
-            GemvArgs a;
-            a.grid = dim3(((N + 15) / 16 + tpw - 1) / tpw, (M + 15) / 16);
-            a.block = dim3(1024);
-            a.lds = lds;
-            a.stream = stream;
-            a.x = (const uint16_t *)x;
-            a.wq = wq;
-            a.scales = scales;
-            a.y = y;
-            a.M = M;
-            a.N = N;
-            a.K = K;
-            a.L = 1;
-            a.tps = tpw;
-            a.plan = plan;
-            a.items = SegItems{};
-            a.items.count = 1;
-            a.items.wg_end[0] = (int)a.grid.x;
-            a.items.wq[0] = wq;
-            a.items.scales[0] = scales;
-            a.items.y[0] = y;
-            a.items.N[0] = N;
-            if (bf16)
-                launch_seg_b<true>(R, LQ, a);
-            else
-                launch_seg_b<false>(R, LQ, a);
-            return hipGetLastError();
-        }
-    }
-    const GemvShape sh = gemv_shape(M, N, plan, K);
-    const int tiles = (N + 15) / 16;
     GemvArgs a;
     if (sh.split) {
         const int W = plan.S / sh.L;
         const int TW = sh.tw;
-        a.grid = dim3((tiles + TW - 1) / TW, (M + 15) / 16);
+        a.grid = dim3((unsigned)fill_items(a.items, items, count, TW), (M + 15) / 16);
         a.block = dim3(64 * W * TW);
     } else {
-        const int streams = (tiles + sh.tps - 1) / sh.tps;
-        a.grid = dim3((streams + 3) / 4, (M + 15) / 16);
+        if (count != 1)
+            return false;
+        const int streams = ((items[0].N + 15) / 16 + sh.tps - 1) / sh.tps;
+        fill_items(a.items, items, 1, 1);
+        a.items.wg_end[0] = (streams + 3) / 4;
+        a.grid = dim3((unsigned)a.items.wg_end[0], (M + 15) / 16);
         a.block = dim3(256);
     }
     a.lds = sh.lds;
     a.stream = stream;
     a.x = (const uint16_t *)x;
-    a.wq = wq;
-    a.scales = scales;
-    a.y = y;
     a.M = M;
-    a.N = N;
     a.K = K;
     a.L = sh.L;
     a.tps = sh.tps;
     a.plan = plan;
+    // accumulator rows per lane: ceil(rows / 4), with 3 rounded up to 4
+    const int rows = M < 16 ? M : 16;
+    const int R = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;
     // every 16-row slice but a last short one has 16 rows
     if (bf16)
         launch_gemv_b<true>(R, sh, a);
     else
         launch_gemv_b<false>(R, sh, a);
-    return hipGetLastError();
+    return true;
 }
 
-bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
-                         hipStream_t stream, hipError_t *err)
+// The segment form over the matrices of `items`, tpw tiles per workgroup.
+static void launch_seg_items(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
+                             const Plan &plan, int LQ, int tpw, size_t lds, hipStream_t stream)
 {
-    const Plan plan = make_plan(K);
-    int LQ;
-    if (count < 1 || count > kGroupMax || !seg_fits_k(M, plan, LQ))
-        return false;
-    // tiles per workgroup from the group's total, about one workgroup per
-    // compute unit over all of them; each matrix gets whole workgroups
-    long long tiles = 0;
-    for (int i = 0; i < count; ++i)
-        tiles += (items[i].N + 15) / 16;
-    const int tpw = (int)((tiles + 255) / 256);
-    const size_t lds = seg_lds_bytes(M, tpw);
-    if (lds > SEG_LDS_MAX)
-        return false;
     GemvArgs a;
-    a.items = SegItems{};
-    a.items.count = count;
-    int wg = 0;
-    for (int i = 0; i < count; ++i) {
-        wg += ((items[i].N + 15) / 16 + tpw - 1) / tpw;
-        a.items.wg_end[i] = wg;
-        a.items.wq[i] = items[i].wq;
-        a.items.scales[i] = items[i].scales;
-        a.items.y[i] = items[i].y;
-        a.items.N[i] = items[i].N;
-    }
-    a.grid = dim3((unsigned)wg, (unsigned)((M + 15) / 16));
+    a.grid = dim3((unsigned)fill_items(a.items, items, count, tpw), (unsigned)((M + 15) / 16));
     a.block = dim3(1024);
     a.lds = lds;
     a.stream = stream;
     a.x = (const uint16_t *)x;
-    a.wq = nullptr;
-    a.scales = nullptr;
-    a.y = nullptr;
     a.M = M;
-    a.N = 0;
     a.K = K;
     a.L = 1;
     a.tps = tpw;
@@ -1644,6 +1666,52 @@ bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int c
         launch_seg_b<true>(R, LQ, a);
     else
         launch_seg_b<false>(R, LQ, a);
+}
+
+hipError_t launch_gemv(const void *x, bool bf16, const uint8_t *wq, const uint16_t *scales,
+                       float *y, int M, int N, int K, hipStream_t stream)
+{
+    const Plan plan = make_plan(K);
+    const GroupItem item{wq, scales, y, N};
+    int LQ, tpw;
+    size_t lds;
+    if (seg_shape(M, N, plan, LQ, tpw, lds))
+        launch_seg_items(x, bf16, &item, 1, M, K, plan, LQ, tpw, lds, stream);
+    else
+        launch_gemv_items(x, bf16, &item, 1, M, K, plan, gemv_shape(M, N, plan, K), stream);
+    return hipGetLastError();
+}
+
+bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
+                         hipStream_t stream, hipError_t *err)
+{
+    if (count < 1 || count > kGroupMax)
+        return false;
+    const Plan plan = make_plan(K);
+    // the group's total width decides the shape, as one matrix that wide
+    long long tiles = 0;
+    for (int i = 0; i < count; ++i)
+        tiles += (items[i].N + 15) / 16;
+    int LQ;
+    if (seg_fits_k(M, plan, LQ)) {
+        // tiles per workgroup from the group's total, about one workgroup
+        // per compute unit over all of them; each matrix gets whole
+        // workgroups
+        const int tpw = (int)((tiles + 255) / 256);
+        const size_t lds = seg_lds_bytes(M, tpw);
+        if (lds <= SEG_LDS_MAX) {
+            launch_seg_items(x, bf16, items, count, M, K, plan, LQ, tpw, lds, stream);
+            *err = hipGetLastError();
+            return true;
+        }
+    }
+    // the split form (a workgroup per column tile of each matrix), unless
+    // the group is wide enough for the streaming form: then one call each
+    if (tiles >= (1LL << 26))
+        return false;
+    const GemvShape sh = gemv_shape(M, (int)(16 * tiles), plan, K);
+    if (!launch_gemv_items(x, bf16, items, count, M, K, plan, sh, stream))
+        return false;
     *err = hipGetLastError();
     return true;
 }

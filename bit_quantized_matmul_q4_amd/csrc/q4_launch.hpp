@@ -20,9 +20,10 @@ struct GroupItem {
     int N;
 };
 
-// The group (1..8 matrices) in one launch of the matrix-vector kernel's
-// segment form.  Returns false, launching nothing, where that form does not
-// apply to K (then *err is untouched); else the launch status in *err.
+// The group (1..8 matrices) in one launch of the matrix-vector kernel: the
+// segment form where it takes K, else the split form.  Returns false,
+// launching nothing, for a group whose total width calls for the streaming
+// form (then *err is untouched); else the launch status in *err.
 bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int count, int M, int K,
                          hipStream_t stream, hipError_t *err);
 
