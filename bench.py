@@ -254,6 +254,33 @@ def main() -> int:
         log("calibration read: %.1f GB/s (%.1f%% of 8 TB/s)" % (calib["gbs"], calib["pct_peak"]))
     records = Records(calib["gbs"] if calib else None)
 
+    # ---- issue overlap of the matrix core and the VALU (probe_issue): per
+    # iteration a wave runs 4 independent bf16 block dots (mode 1), 16
+    # independent fp32 FMAs (mode 2) or both (mode 3); cycles per iteration
+    # of one SIMD at 2.4 GHz, 1 and 4 waves per SIMD.  Both together taking
+    # about the sum of the two alone means their issue does not overlap,
+    # which bounds the matrix-matrix kernel (its per-block fmaf and
+    # subtraction are VALU work on top of every block dot).
+    issue = None
+    if not (args.headline_only or args.eager_step):
+        plib.q4probe_issue.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        plib.q4probe_issue.restype = ctypes.c_int
+        iters = 4000
+        issue = {"iterations": iters, "work_per_wave_iteration": "4 v_mfma_f32_16x16x32_bf16 + 16 v_fma_f32",
+                 "cycles_per_iteration_per_simd": {}}
+        for wps in (1, 4):
+            pout = torch.empty(256 * wps * 256, dtype=torch.float32, device=dev)
+            row = {}
+            for mode, name in ((1, "mfma_only"), (2, "valu_only"), (3, "both")):
+                def run(mode=mode, wps=wps, pout=pout):
+                    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                    assert plib.q4probe_issue(mode, pout.data_ptr(), 256 * wps, iters, st) == 0
+                us = best_per_call(run, 1, tries=3)
+                row[name] = round(us * 1e-6 * 2.4e9 / iters, 1)
+            issue["cycles_per_iteration_per_simd"]["%d_waves_per_simd" % wps] = row
+            del pout
+        log("issue overlap (cycles per iteration per SIMD): %s" % issue["cycles_per_iteration_per_simd"])
+
     # ---- inputs, resident in HBM: weights drawn directly in the packed form.
     # Each copy of the set is held as the fused buffers (q|k|v, gate|up,
     # down); the six projections are views into them.
@@ -835,7 +862,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "detail": {"calibration_read": calib, "parity": parity,
                    "per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "per_launch_us": per_launch_us,
-                   "grouped_step": grouped_step, "fused_step": fused_step, "mixed_124": mixed,
+                   "grouped_step": grouped_step, "fused_step": fused_step, "mixed_124": mixed, "issue_overlap": issue,
                    "decode_stream_7b": stream, "small_workloads": small or None, "switching_schemes": schemes,
                    "crossover": crossover, "records": records.rows},
     }

@@ -8,6 +8,9 @@
 // slot or on other rows), run-to-run determinism, the nibble dequantization
 // and the corrected block dot.  Not part of the product library.
 //
+// probe_issue times a wave's block dots, FMAs, or both interleaved, for
+// the benchmark's check of how far the matrix core and the VALU overlap.
+//
 // probe_read is a plain streaming read of a device buffer: the benchmark's
 // yardstick of the bandwidth the memory system delivers to a simple kernel
 // ("a big copy, not the spec sheet", in "Why LLM Decoding Is Slow, and Why
@@ -85,9 +88,67 @@ __global__ __launch_bounds__(512) void probe_read(const q4::u32x4 *__restrict__ 
         sink[0] = r;
 }
 
+// Issue-overlap probe: per iteration a wave runs 4 independent bf16 block
+// dots (v_mfma_f32_16x16x32_bf16 into 4 accumulators) when MODE & 1 and 16
+// independent fp32 FMAs (8 chains) when MODE & 2, so the time of MODE 3
+// against MODES 1 and 2 tells whether the matrix core and the VALU of the
+// waves on a SIMD work in parallel.  One value per thread goes to out (so
+// nothing is dropped).
+template <int MODE>
+__global__ __launch_bounds__(256) void probe_issue(float *out, int iters, float s)
+{
+    const int t = threadIdx.x;
+    const q4::u32x4 a = {0x3F803F80u + t, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const q4::u32x4 b = {0x3F803F80u, 0x3F803F80u + t, 0x3F803F80u, 0x3F803F80u};
+    q4::f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = (float)(t + j);
+    for (int i = 0; i < iters; ++i) {
+        if constexpr ((MODE & 1) != 0) {
+            const q4::bf16x8 A = __builtin_bit_cast(q4::bf16x8, a), B = __builtin_bit_cast(q4::bf16x8, b);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, c3, 0, 0, 0);
+        }
+        if constexpr ((MODE & 2) != 0) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[j] = __builtin_fmaf(v[j], s, 1.0f);
+        }
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                     "+v"(v[7]));
+    }
+    float r = c0.x + c1.y + c2.z + c3.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        r += v[j];
+    out[blockIdx.x * 256 + t] = r;
+}
+
 }  // namespace
 
 extern "C" {
+
+// The issue-overlap probe (mode 1: block dots only, 2: FMAs only, 3: both)
+// with `blocks` workgroups of 4 waves; out holds 256 blocks floats.
+int q4probe_issue(int mode, void *out, int blocks, int iters, void *stream)
+{
+    if (!out || blocks < 1 || iters < 1 || mode < 1 || mode > 3)
+        return -1;
+    hipStream_t st = (hipStream_t)stream;
+    if (mode == 1)
+        hipLaunchKernelGGL(probe_issue<1>, dim3(blocks), dim3(256), 0, st, (float *)out, iters, 0.5f);
+    else if (mode == 2)
+        hipLaunchKernelGGL(probe_issue<2>, dim3(blocks), dim3(256), 0, st, (float *)out, iters, 0.5f);
+    else
+        hipLaunchKernelGGL(probe_issue<3>, dim3(blocks), dim3(256), 0, st, (float *)out, iters, 0.5f);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Streams `bytes` (a multiple of 16, src 16-byte aligned) with `blocks`
 // workgroups of 512 threads.
