@@ -183,12 +183,12 @@ int q4_pack_nibbles(const uint8_t *Wq_rows, const void *scales, uint8_t *Wq, voi
  * the reduction order depends on K only.  One launch of the matrix-vector
  * kernel when the crossover rule picks it for the group (as q4_linear_ex
  * with Q4_AUTO and this workspace would for each matrix), unless the group
- * is too wide for one launch (65536 columns or more in all, for K outside
- * 2048..6144); else one call per matrix as q4_linear_ex with Q4_AUTO and the
- * given workspace (optional, as for q4_linear_ex; the calls run in stream
- * order, so one workspace of the largest item's q4_workspace_bytes serves
- * them all).  All argument checks (every item's) run before any HIP call.
- * No allocation.
+ * is too wide for one launch (65536 columns or more in all where the
+ * segment form, 2048 <= K <= 6144, does not take it); else one call per
+ * matrix as q4_linear_ex with Q4_AUTO and the given workspace (optional, as
+ * for q4_linear_ex; the calls run in stream order, so one workspace of the
+ * largest item's q4_workspace_bytes serves them all).  All argument checks
+ * (every item's) run before any HIP call.  No allocation.
  */
 #define Q4_GROUP_MAX 8
 typedef struct q4_group_item {
