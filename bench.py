@@ -281,6 +281,25 @@ def main() -> int:
             del pout
         log("issue overlap (cycles per iteration per SIMD): %s" % issue["cycles_per_iteration_per_simd"])
 
+    # ---- the fixed cost of a launch: a graph of 48 back-to-back empty kernels
+    # (1 and 256 workgroups), us per launch.  The step's 48 launches pay it
+    # before any work.
+    launch_floor = None
+    if not (args.headline_only or args.eager_step):
+        plib.q4probe_empty.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        plib.q4probe_empty.restype = ctypes.c_int
+        esink = torch.zeros(256, dtype=torch.int32, device=dev)
+        launch_floor = {}
+        for nb in (1, 256):
+            def empties(nb=nb):
+                st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for _ in range(48):
+                    assert plib.q4probe_empty(esink.data_ptr(), nb, 0, st) == 0
+            launch_floor["%d_workgroups_us" % nb] = round(best_per_call(empties, 48, tries=5), 3)
+        launch_floor["step_launches"] = 48
+        launch_floor["us_per_step"] = round(48 * launch_floor["1_workgroups_us"], 1)
+        log("empty-kernel launch floor: %s" % launch_floor)
+
     # ---- inputs, resident in HBM: weights drawn directly in the packed form.
     # Each copy of the set is held as the fused buffers (q|k|v, gate|up,
     # down); the six projections are views into them.
@@ -862,7 +881,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "detail": {"calibration_read": calib, "parity": parity,
                    "per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "per_launch_us": per_launch_us,
-                   "grouped_step": grouped_step, "fused_step": fused_step, "mixed_124": mixed, "issue_overlap": issue,
+                   "grouped_step": grouped_step, "fused_step": fused_step, "mixed_124": mixed, "issue_overlap": issue, "launch_floor": launch_floor,
                    "decode_stream_7b": stream, "small_workloads": small or None, "switching_schemes": schemes,
                    "crossover": crossover, "records": records.rows},
     }

@@ -130,9 +130,27 @@ __global__ __launch_bounds__(256) void probe_issue(float *out, int iters, float 
     out[blockIdx.x * 256 + t] = r;
 }
 
+// An empty kernel (one store that never happens): the benchmark's measure of
+// the fixed cost of one launch in a graph.
+__global__ __launch_bounds__(256) void probe_empty(uint32_t *sink, int v)
+{
+    if (v == 0x5EED && threadIdx.x == 0)
+        sink[blockIdx.x] = (uint32_t)v;
+}
+
 }  // namespace
 
 extern "C" {
+
+// `blocks` workgroups of 256 threads that do nothing (sink is never written
+// for v != 0x5EED; it must hold `blocks` words if v == 0x5EED).
+int q4probe_empty(void *sink, int blocks, int v, void *stream)
+{
+    if (!sink || blocks < 1)
+        return -1;
+    hipLaunchKernelGGL(probe_empty, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint32_t *)sink, v);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // The issue-overlap probe (mode 1: block dots only, 2: FMAs only, 3: both)
 // with `blocks` workgroups of 4 waves; out holds 256 blocks floats.
