@@ -1331,8 +1331,9 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     // Measured on MI355X (7B and 0.5B shapes, M = 1..8): very wide N streams
     // one tile per wave over all of K; otherwise a column tile is split over
     // runs of segments of about 4 quads up to 4 rows or for K <= 1024
-    // (896 x 896 3.8 -> 3.3 us, k_proj 4.3 -> 4.1 us), else 7 (q_proj at
-    // 8 rows 5.3 us against 5.5 with 4); 14 for wide N at one or two rows.
+    // (k_proj 4.3 -> 4.1 us), else 7 (q_proj at 8 rows 5.3 us against 5.5
+    // with 4); 14 for wide N at one or two rows; one segment for K < 1024
+    // (below).
     sh.split = tiles < 4096;
     int L = 1;
     const int target = (tiles >= 1024 && M <= 2) ? 14 : (M <= 4 || plan.G <= 8) ? 4 : 7;  // quads per run
@@ -1346,6 +1347,12 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     // 6.0 us, 6144 x 4864 8.2 -> 6.9 us)
     if (tiles > 256 && tiles <= 512 && plan.G > 16 && plan.G <= 48)
         L = plan.S / 4;
+    // K < 1024 (at most 4 segments of under 2 quads): one segment a run up
+    // to 256 tiles, and for wider N up to 4 rows (measured: 896 x 896 at one
+    // row 3.46 -> 3.21 us, 512 x 512 3.52 -> 3.06 us, 4864 x 896 4.18 ->
+    // 4.05 us; not from 8 rows on at 304 tiles and more, nor at K = 1024)
+    if (plan.S <= 4 && (tiles <= 256 || M <= 4))
+        L = 1;
     sh.L = L;
     sh.tps = (tiles + 2047) / 2048;  // about 2048 streams
     sh.D = 8;
