@@ -1330,13 +1330,13 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     const int tiles = (N + 15) / 16;
     // Measured on MI355X (7B and 0.5B shapes, M = 1..8): very wide N streams
     // one tile per wave over all of K; otherwise a column tile is split over
-    // runs of segments of about 4 quads up to 4 rows or for K <= 1024
-    // (k_proj 4.3 -> 4.1 us), else 7 (q_proj at 8 rows 5.3 us against 5.5
-    // with 4); 14 for wide N at one or two rows; one segment for K < 1024
-    // (below).
+    // runs of segments of about 4 quads up to 8 rows or for K <= 1024
+    // (k_proj 4.3 -> 4.1 us at one row; at 8 rows k_proj 5.04 -> 4.82 us and
+    // q_proj 5.48 -> 5.35 us against runs of 7), else 7; 14 for wide N at one
+    // or two rows; one segment for K < 1024 (below).
     sh.split = tiles < 4096;
     int L = 1;
-    const int target = (tiles >= 1024 && M <= 2) ? 14 : (M <= 4 || plan.G <= 8) ? 4 : 7;  // quads per run
+    const int target = (tiles >= 1024 && M <= 2) ? 14 : (M <= 8 || plan.G <= 8) ? 4 : 7;  // quads per run
     while (L < plan.S && ((2 * L * plan.G) >> plan.log2S) <= target)
         L *= 2;
     while (plan.S / L > 8)
