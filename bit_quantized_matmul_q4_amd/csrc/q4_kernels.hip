@@ -1348,10 +1348,11 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     if (tiles > 256 && tiles <= 512 && plan.G > 16 && plan.G <= 48)
         L = plan.S / 4;
     // K < 1024 (at most 4 segments of under 2 quads): one segment a run up
-    // to 256 tiles, and for wider N up to 4 rows (measured: 896 x 896 at one
-    // row 3.46 -> 3.21 us, 512 x 512 3.52 -> 3.06 us, 4864 x 896 4.18 ->
-    // 4.05 us; not from 8 rows on at 304 tiles and more, nor at K = 1024)
-    if (plan.S <= 4 && (tiles <= 256 || M <= 4))
+    // to 256 tiles, and up to 512 tiles at up to 4 rows (measured: 896 x 896
+    // at one row 3.46 -> 3.21 us, 512 x 512 3.52 -> 3.06 us, 4864 x 896 4.18
+    // -> 4.05 us; not from 8 rows on at 304 tiles and more, not for the
+    // 680-tile grouped 0.5B layer, nor at K = 1024)
+    if (plan.S <= 4 && (tiles <= 256 || (M <= 4 && tiles <= 512)))
         L = 1;
     sh.L = L;
     sh.tps = (tiles + 2047) / 2048;  // about 2048 streams
