@@ -1371,14 +1371,16 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     // Measured on MI355X, weights streaming from HBM.  Split form up to 8
     // rows: with eight runs a tile (K = 4096, 4864, 8192, 18944) x through
     // per-wave slots (down_proj at 4 / 8 rows 11.9 / 15.8 -> 10.6 / 13.3 us
-    // against the staged / ring forms), otherwise x gathered by DPP (at 1-4
+    // against the staged / ring forms), and so for more than 256 tiles up to
+    // 4 rows or from K = 1024 (against DPP gathering: 4608 x 3584 at 4 rows
+    // 6.24 -> 5.98 us, 6144 x 4864 7.6 -> 7.2 us, 4864 x 896 4.13 -> 3.99
+    // us; not 8192 x 512 at 5-8 rows), otherwise x gathered by DPP (at 1-4
     // rows against staging: 4864 x 896 4.3 -> 3.8 us, 2048 x 2048 3.9 ->
-    // 3.6 us, 4608 x 3584 6.1 -> 5.8 us; at 5-8 rows against the ring:
-    // k_proj 4.75 -> 4.67 us).  One stream per wave (very wide N): x staged
-    // up to 4 rows, else in the ring.
+    // 3.6 us; at 5-8 rows against the ring: k_proj 4.75 -> 4.67 us).  One
+    // stream per wave (very wide N): x staged up to 4 rows, else in the ring.
     sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
     if (sh.split && M <= 8)
-        sh.xm = plan.S / sh.L == 8 ? XM_WAVE : XM_QUAD;
+        sh.xm = plan.S / sh.L == 8 || (tiles > 256 && (M <= 4 || plan.G >= 8)) ? XM_WAVE : XM_QUAD;
     sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
     if (sh.xm != XM_LDS && sh.split)
         sh.D = 4;  // x rides in the ring: up to 22 registers a stage
