@@ -606,12 +606,27 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // segment's length are placeholders: their loads fall outside the
 // resources' ranges (zero, no memory access) and they compute nothing.
 // With one combine (tpw <= TC) the combine writes y directly.
+//
+// Memory instructions, not bytes, set much of the cost here (measured on
+// MI355X, gate at one row: a scale load per stage costs ~0.7 us even when it
+// hits the cache), so two inputs are fetched in few of them:
+//  * up to four rows (R = 1) the workgroup stages x in LDS, one 16-byte load
+//    a thread and 16 KB (waves past x's bytes issue none), and each wave
+//    reads its A operands from there (lanes of row slots past the batch read
+//    nothing); with more rows each wave loads its own, four 16-byte loads a
+//    quad (gate at one row 10.1 -> 9.7 us, gate|up 17.6 -> 16.6 us);
+//  * with whole ring rounds of four stages (LQ <= 2, R <= 2) the scales come
+//    in groups of four positions, one 8-byte load a lane for the group: the
+//    lanes of row g load position g's column scales and each position's reach
+//    every row by ds_bpermute (gate 10.1 -> 9.9 us, gate|up 17.6 -> 16.8 us,
+//    both together 10.1 -> 9.4 us at one to four rows).
 // grid = (sum over the matrices of ceil(tiles / tpw), ceil(M / 16)),
 // block = 1024; a workgroup's matrix is the one whose range of workgroup
 // ids holds it (see MatrixItems).  With MR =
 // min(M, 16), dynamic LDS: roots [NB][TC][16 seg][MR][16] floats (NB = 1
 // if tpw <= TC: one combine after the last tile; else 2, double-buffered),
-// then outputs [tpw][MR][16] floats.
+// then outputs [tpw][MR][16] floats, then (R = 1) x, M rows of 2 K bytes
+// and 256 bytes of slack (seg_lds_bytes).
 // TC: tiles per combine.  Measured on MI355X: with up to 8 tiles per
 // workgroup one combine at the end is fastest (gate at one row 10.7 ->
 // 10.4 us, at 9 rows 13.2 -> 12.4 us); with more tiles (gate|up, the LM
@@ -649,6 +664,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     const int MR = min(M, 16);
     float *roots = seg_lds;                                         // [NB][TC][16 seg][MR][16]
     float *ystage = seg_lds + seg_nbuf(TC, tpw) * TC * 16 * MR * 16;  // [tpw][MR][16]
+    uint8_t *x_lds = (uint8_t *)(ystage + tpw * MR * 16);              // R = 1: [mrows][2 K bytes]
 
     const MatrixSel sel = select_matrix(items);
     const uint8_t *__restrict__ wq = sel.wq;
@@ -668,18 +684,31 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     const int qs = (j * G) >> 4;
     const int len = (((j + 1) * G) >> 4) - qs;  // 1 .. LQ quads
 
-    // this segment's A operands, once
+    // this segment's A operands, once: staged through LDS up to four rows,
+    // else loaded by the wave
+    constexpr bool XLDS = R == 1;
+    constexpr int XV = 3;  // 16-byte chunks a thread: 4 rows x 6144 x 2 bytes / 16 KB
     const uint32_t x_bytes = (uint32_t)mrows * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
     const int xr = slot_row(c);  // (as in q4_gemv)
     const uint32_t x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
+    const uint32_t x_wave = (uint32_t)(threadIdx.x & ~63u) * 16u;  // the wave's first chunk byte
     u32x4 xs[LQ][4];
+    u32x4 xv[XV];
+    if constexpr (XLDS) {
 #pragma unroll
-    for (int q = 0; q < LQ; ++q)
+        for (int u = 0; u < XV; ++u)
+            if (x_wave + 16384u * u < x_bytes)  // wave-uniform: whole waves past x issue nothing
+                xv[u] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 16u * threadIdx.x + 16384u * u, 0, 0));
+    } else {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            xs[q][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rx, x_lane + 64u * b + 256u * (qs + min(q, len - 1)), 0, 0));
+        for (int q = 0; q < LQ; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                xs[q][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rx, x_lane + 64u * b + 256u * (qs + min(q, len - 1)), 0, 0));
+    }
 
     // the stream: tiles t_first .. t_first + ntiles - 1, quads qs .. qs + LQ - 1
     const uint32_t tile_b = (uint32_t)G * 1024u, tile_s = (uint32_t)G * 128u;
@@ -693,6 +722,22 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     // the output stage, stored at the end
     const bool one_chunk = tpw <= TC;
 
+    // scale groups (whole ring rounds of four stages): the lanes of row g
+    // load the column scales of position gpos + g (placeholders and positions
+    // past the stream fall outside the range: zero, no memory access)
+    constexpr bool SG = D == 4 && LQ <= 2 && R <= 2;
+    auto load_group = [&](int gpos) -> u32x2 {
+        const int pp = gpos + g;
+        const int i = pp / LQ, q = pp % LQ;
+        const uint32_t so = q < len && pp < npos ? (uint32_t)i * tile_s + 128u * (qs + q) : s_range;
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane + so, 0, kWeightLoadPolicy));
+    };
+    u32x2 sg_cur{0u, 0u}, sg_next{0u, 0u};
+    if constexpr (SG) {
+        sg_next = load_group(0);
+        issue_fence();
+    }
+
     GemvStage ring[D];
     // position -> (tile, quad); live unless the quad is past the segment or
     // the tile past the workgroup's
@@ -702,14 +747,39 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         const uint32_t wo = live ? (uint32_t)i * tile_b + 1024u * (qs + q) : w_range;
         const uint32_t so = live ? (uint32_t)i * tile_s + 128u * (qs + q) : s_range;
         st.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + wo, 0, kWeightLoadPolicy));
-        st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane + so, 0, kWeightLoadPolicy));
+        if constexpr (!SG)
+            st.s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s_lane + so, 0, kWeightLoadPolicy));
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         load(ring[d], d, d % LQ);
         issue_fence();
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): x and the prefill (see q4_gemv)
+    // (no wait for the whole prefill here: the first stage's wait covers x,
+    // loaded before it; measured: gate 10.3 -> 10.1 us)
+    if constexpr (XLDS) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const uint32_t o = 16u * threadIdx.x + 16384u * u;
+            if (x_wave + 16384u * u < x_bytes && o < x_bytes)
+                *(u32x4 *)(x_lds + o) = xv[u];
+        }
+        workgroup_barrier_lds();
+        // blocks of a short last quad past the row read the next row or the
+        // slack (their block dots are skipped)
+        const uint8_t *xrow = x_lds + (uint32_t)xr * (uint32_t)K * 2u + 16u * g;
+#pragma unroll
+        for (int q = 0; q < LQ; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                xs[q][b] = u32x4{0u, 0u, 0u, 0u};
+        if (xr < mrows)
+#pragma unroll
+            for (int q = 0; q < LQ; ++q)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    xs[q][b] = *(const u32x4 *)(xrow + 64u * b + 256u * (qs + min(q, len - 1)));
+    }
 
     const Dequant<BF16> dq;
     // bf16: the segment's correction dots once, for all the wave's tiles,
@@ -737,10 +807,16 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         const int i = pos / LQ;
         if (q < len) {
             const int nq = SHORT && qs + q == G - 1 ? plan.nb - 4 * (G - 1) : 4;
+            GemvStage &st = ring[d];
+            if constexpr (SG) {  // position d of the group: its scales from row d
+                const int src = (16 * d + c) << 2;
+                st.s.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.x);
+                st.s.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.y);
+            }
             if constexpr (HOIST)
-                gemv_quad_pre<BF16, R, SHORT>(ring[d], xs[q], Eh[q], nq, dq, p);
+                gemv_quad_pre<BF16, R, SHORT>(st, xs[q], Eh[q], nq, dq, p);
             else
-                gemv_quad<BF16, R, SHORT>(ring[d], xs[q], nq, dq, p);
+                gemv_quad<BF16, R, SHORT>(st, xs[q], nq, dq, p);
         }
         if (q == LQ - 1) {  // the tile's segment partial is done
             float *rt = roots + ((((i / TC) & 1) * TC + i % TC) * 16 + j) * (MR * 16);
@@ -786,14 +862,23 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
         // compiler has to allow for a round that skips stages and still
         // loops, and its waits for the ring then drain more of it than the
         // round needs (measured: gate 11.8 -> 11.5 us at M = 1).
+        // (scale groups: one per round, the next loaded a round ahead)
         int base = 0;
         for (; base + D <= npos; base += D) {
+            if constexpr (SG) {
+                sg_cur = sg_next;
+                issue_fence();
+                sg_next = load_group(base + D);
+                issue_fence();
+            }
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 compute(d, base + d);
                 refill(d, base + d);
             }
         }
+        if constexpr (SG)
+            sg_cur = sg_next;
 #pragma unroll
         for (int d = 0; d < D - LQ; ++d)
             if (base + d < npos) {
@@ -1608,11 +1693,13 @@ static bool seg_fits_k(int M, const Plan &plan, int &LQ)
     return !(LQ > 3 || (LQ == 3 && M > 8));
 }
 
-static size_t seg_lds_bytes(int M, int tpw)
+static size_t seg_lds_bytes(int M, int K, int tpw)
 {
     const int MR = M < 16 ? M : 16;
     const int tc = seg_tc(M, tpw);
-    return (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw);
+    // up to four rows x is staged too (2 K bytes a row and 256 of slack)
+    const size_t x = M <= 4 ? (size_t)M * K * 2 + 256 : 0;
+    return (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw) + x;
 }
 
 static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t &lds)
@@ -1628,7 +1715,7 @@ static bool seg_shape(int M, int N, const Plan &plan, int &LQ, int &tpw, size_t 
     if (tiles <= 256 || (tiles <= 512 && (LQ == 3 || (LQ == 2 && M <= 4))))
         return false;
     tpw = (tiles + 255) / 256;
-    lds = seg_lds_bytes(M, tpw);
+    lds = seg_lds_bytes(M, plan.nb * 32, tpw);
     return lds <= SEG_LDS_MAX;
 }
 
@@ -1724,7 +1811,7 @@ bool launch_gemv_grouped(const void *x, bool bf16, const GroupItem *items, int c
         // per compute unit over all of them; each matrix gets whole
         // workgroups
         const int tpw = (int)((tiles + 255) / 256);
-        const size_t lds = seg_lds_bytes(M, tpw);
+        const size_t lds = seg_lds_bytes(M, K, tpw);
         if (lds <= SEG_LDS_MAX) {
             launch_seg_items(x, bf16, items, count, M, K, plan, LQ, tpw, lds, stream);
             *err = hipGetLastError();
