@@ -183,13 +183,30 @@ __device__ __forceinline__ void issue_fence()
 // refill past the stream's end): the four A-operand blocks (XM_RING) or NW
 // loads of four rows each (XM_WAVE, into xa[0 .. NW - 1]).
 template <int XM, int NW>
+__device__ __forceinline__ void gemv_load_x(GemvStage &st, GemvStream &in, uint32_t x_off)
+{
+    if constexpr (XM == XM_RING) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            st.xa[b] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b + x_off, 0, 0));
+    } else if constexpr (XM == XM_WAVE || XM == XM_QUAD) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j] + x_off, 0, 0));
+    }
+}
+
+template <int XM, int NW, bool LS = true, bool LX = true>
 __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
     st.w = __builtin_bit_cast(u32x4,
                               __builtin_amdgcn_raw_buffer_load_b128(in.w, in.w_lane + in.w_off, 0, kWeightLoadPolicy));
-    st.s = __builtin_bit_cast(u32x2,
-                              __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane + in.s_off, 0, kWeightLoadPolicy));
-    if constexpr (XM == XM_RING) {
+    if constexpr (LS)  // else the scales come in groups (q4_gemv)
+        st.s = __builtin_bit_cast(u32x2,
+                                  __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane + in.s_off, 0, kWeightLoadPolicy));
+    if constexpr (!LX) {
+    } else if constexpr (XM == XM_RING) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
@@ -339,7 +356,7 @@ __device__ __forceinline__ MatrixSel select_matrix(const MatrixItems<NM> items)
 // Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
 // (XM_LDS) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of
 // slack, or (XM_WAVE) one slot of 4 R rows of XW_ROW bytes per wave.
-template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM>
+template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM, bool XF>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x, MatrixItems<NM> items,
                                                               int M, int K, Plan plan, int L, int tps)
 {
@@ -394,7 +411,16 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     GemvStream in;
     in.w = buffer_rsrc(wq + ((size_t)min(t0, n16 - 1) * G + q0) * 1024, (uint32_t)total * 1024u);
     in.s = buffer_rsrc(scales + ((size_t)min(t0, n16 - 1) * G + q0) * 64, (uint32_t)total * 128u);
-    in.x = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
+    if constexpr (XF) {
+        // x's loads stay where they are written (the compiler may otherwise
+        // move loads of a read-only argument down to their first use, here
+        // behind the wait for the prefill)
+        const uint16_t *xs_base = x + (size_t)m0 * K;
+        asm volatile("" : "+s"(xs_base));
+        in.x = buffer_rsrc(xs_base, x_bytes);
+    } else {
+        in.x = buffer_rsrc(x + (size_t)m0 * K, x_bytes);
+    }
     in.w_lane = 16u * lane;
     in.s_lane = 8u * c;
     // row slots past the batch read nothing (an offset past the resource's
@@ -458,9 +484,41 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     GemvStage ring[D];
     int ql = q0;     // quad of the next stage to load
     int left = total;  // loads left that the stream uses
+    // Scale groups (four-stage rings): one 8-byte load a lane for four
+    // consecutive stream quads, the lanes of row g loading quad g's column
+    // scales; each stage takes its quad's from that row by ds_bpermute (as in
+    // the segment form).  Groups past the stream read nothing.
+    constexpr bool SG = D == 4;
+    uint32_t sg_off = 0;
+    auto load_group = [&]() -> u32x2 {
+        const u32x2 v = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(in.s, in.s_lane + 128u * g + sg_off, 0, kWeightLoadPolicy));
+        sg_off += 512;
+        return v;
+    };
+    u32x2 sg_cur{0u, 0u}, sg_next{0u, 0u};
+    if constexpr (SG) {
+        sg_next = load_group();
+        issue_fence();
+    }
+    // XF (one row): the prefill's x first, then its codes.  Otherwise the x
+    // of each prefill stage is written with its codes but the compiler issues
+    // it after the wait below (see XF), one round trip to cache later.
+    // Measured on MI355X: at one row x first is faster (down_proj 10.8 ->
+    // 9.8 us), from two rows x after the codes (k_proj at 8 rows 5.2 -> 4.7 us).
+    if constexpr (XF) {
+        int qx = ql, lx = left;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            gemv_load_x<XM, R>(ring[d], in, lx > 0 ? 256u * qx : x_bytes);
+            qx = qx + 1 == q1 ? q0 : qx + 1;
+            --lx;
+        }
+        issue_fence();
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {  // in stage order (see the refill below)
-        gemv_load<XM, R>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+        gemv_load<XM, R, !SG, !XF>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
         ql = ql + 1 == q1 ? q0 : ql + 1;
         --left;
         issue_fence();
@@ -496,6 +554,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     if constexpr (XL)
         gemv_x_lds(xb[0], xrow, q0);
     for (int base = 0; base < total; base += D) {
+        if constexpr (SG) {  // the round's group; all four stages' scales at once
+            sg_cur = sg_next;
+            issue_fence();
+            sg_next = load_group();
+            issue_fence();
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int src = (16 * d + c) << 2;
+                ring[d].s.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.x);
+                ring[d].s.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.y);
+            }
+        }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int ii = base + d;
@@ -546,7 +616,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             // ranges: they return zero without a memory access, so the
             // wave's end does not wait one more round trip for them.
             issue_fence();
-            gemv_load<XM, R>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+            gemv_load<XM, R, !SG>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
             ql = ql + 1 == q1 ? q0 : ql + 1;
             --left;
             issue_fence();
@@ -1525,21 +1595,33 @@ static void launch_gemv_n(const GemvArgs &a)
     if constexpr (XL == XM_LDS) {
         static const bool lds_raised = [] {
             // a failure here leaves the default limit; the launch then reports it
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL, NM>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL, NM, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL, NM>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL, NM, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
             return true;
         }();
         (void)lds_raised;
     }
     const MatrixItems<NM> items = narrow_items<NM>(a.items);
+    // x first in the prefill at one row (x in the ring)
+    if constexpr (R == 1 && XL != XM_LDS) {
+        if (a.M == 1) {
+            if (a.plan.nb & 3)
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, true>), a.grid, a.block, a.lds, a.stream,
+                                   a.x, items, a.M, a.K, a.plan, a.L, a.tps);
+            else
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, true>), a.grid, a.block, a.lds, a.stream,
+                                   a.x, items, a.M, a.K, a.plan, a.L, a.tps);
+            return;
+        }
+    }
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
-                           a.M, a.K, a.plan, a.L, a.tps);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, false>), a.grid, a.block, a.lds, a.stream, a.x,
+                           items, a.M, a.K, a.plan, a.L, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM>), a.grid, a.block, a.lds, a.stream, a.x, items,
-                           a.M, a.K, a.plan, a.L, a.tps);
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, false>), a.grid, a.block, a.lds, a.stream, a.x,
+                           items, a.M, a.K, a.plan, a.L, a.tps);
 }
 
 // A group's table only for the split form (the streaming form runs one
