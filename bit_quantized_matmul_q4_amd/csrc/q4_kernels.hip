@@ -110,6 +110,25 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
     }
 }
 
+// The block values of a quad (bv[i][r]: block i, accumulator row r), the
+// part of gemv_quad before its scale-accumulates.
+template <bool BF16, int R>
+__device__ __forceinline__ void gemv_block_values(const GemvStage &st, const u32x4 (&xa)[4], const Dequant<BF16> &dq,
+                                                  float (&bv)[4][R])
+{
+    const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 D = blockdot<BF16>(xa[i], dq(w[i]));
+        f32x4 E = D;
+        if constexpr (kCorrected<BF16>)
+            E = blockdot<BF16>(xa[i], dq.offset);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            bv[i][r] = block_value<BF16>(D[r], E[r]);
+    }
+}
+
 // gemv_quad with the quad's correction dots already computed (Eq[i][r]: the
 // value E of block i for accumulator row r), for waves that hold their x
 // for many tiles: E depends on x only, so the same instruction on the same
@@ -553,7 +572,98 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     u32x4 xb[2][4];  // XL: x of the quad being computed and of the next
     if constexpr (XL)
         gemv_x_lds(xb[0], xrow, q0);
-    for (int base = 0; base < total; base += D) {
+    // after quad qc's scale-accumulates: at a segment's end, fold it into the
+    // run's subtree
+    auto finish_quad = [&](int qn) {
+        if (qc + 1 == seg_end) {
+            if (stack.push(p, li, L)) {
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        root[r] = p[r];
+                } else {  // the tile's root, kept in LDS until the stream ends
+                    float *o = ystage + ((wave * tps + t) * 16 + g) * 16 + c;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        o[64 * r] = p[r];
+                    ++t;
+                }
+                li = 0;
+            } else {
+                ++li;
+            }
+            seg_end = ((seg0 + li + 1) * G) >> plan.log2S;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                p[r] = 0.f;
+        }
+        qc = qn;
+    };
+    // A split-form run that the prefill holds whole (total <= D: q, k and v
+    // of the 7B set): every stage's A operands and block dots first, so that
+    // the stages' LDS and matrix-core latencies overlap (such runs often have
+    // a SIMD to themselves), then the scale-accumulates in order.  Measured
+    // on MI355X: a stage costs ~0.25 us of latency one after the other; up to
+    // 4 rows this takes q_proj 4.9 -> 4.6 us, k_proj 4.3 -> 4.0 us and 896 x
+    // 896 3.3 -> 3.2 us (at 8 rows the registers it needs cost more than it
+    // saves).
+    const bool whole = SPLIT && !XL && R == 1 && total <= D;
+    if (whole) {
+        if constexpr (SG) {
+            sg_cur = sg_next;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int src = (16 * d + c) << 2;
+                ring[d].s.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.x);
+                ring[d].s.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.y);
+            }
+        }
+        float bv[D][4][R];
+        auto stage_values = [&](int d) {
+            u32x4 xa[4];
+            if constexpr (XM == XM_WAVE)
+                gemv_x_wave<R>(xa, ring[d], wput, xget);
+            else if constexpr (XM == XM_QUAD)
+                gemv_x_quad<R>(xa, ring[d]);
+            else
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    xa[b] = ring[d].xa[b];
+            gemv_block_values<BF16, R>(ring[d], xa, dq, bv[d]);
+        };
+        // (a run one stage short of the ring computes the spare stage on
+        // zeros rather than branch around it: no branch splits the stages'
+        // instructions, q_proj 4.73 -> 4.60 us)
+        if (total >= D - 1) {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                stage_values(d);
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (d < total)
+                    stage_values(d);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d < total) {
+                const int nq = SHORT ? min(4, plan.nb - 4 * qc) : 4;
+                const uint32_t h[4] = {ring[d].s.x & 0xFFFFu, ring[d].s.x >> 16, ring[d].s.y & 0xFFFFu,
+                                       ring[d].s.y >> 16};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (!SHORT || i < nq) {
+                        const float sc = half_bits_to_float(h[i]);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            p[r] = __builtin_fmaf(sc, bv[d][i][r], p[r]);
+                    }
+                }
+                finish_quad(qc + 1 == q1 ? q0 : qc + 1);
+            }
+        }
+    }
+    for (int base = 0; base < (whole ? 0 : total); base += D) {
         if constexpr (SG) {  // the round's group; all four stages' scales at once
             sg_cur = sg_next;
             issue_fence();
@@ -585,29 +695,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
                     gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
                                               SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
                 }
-                if (qc + 1 == seg_end) {  // segment done: fold into the run's subtree
-                    if (stack.push(p, li, L)) {
-                        if constexpr (SPLIT) {
-#pragma unroll
-                            for (int r = 0; r < R; ++r)
-                                root[r] = p[r];
-                        } else {  // the tile's root, kept in LDS until the stream ends
-                            float *o = ystage + ((wave * tps + t) * 16 + g) * 16 + c;
-#pragma unroll
-                            for (int r = 0; r < R; ++r)
-                                o[64 * r] = p[r];
-                            ++t;
-                        }
-                        li = 0;
-                    } else {
-                        ++li;
-                    }
-                    seg_end = ((seg0 + li + 1) * G) >> plan.log2S;
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        p[r] = 0.f;
-                }
-                qc = qn;
+                finish_quad(qn);
             }
             // refill D quads ahead.  The scheduling barrier keeps the refill
             // after the stage's use: hoisted above it, the refill's wait (the
