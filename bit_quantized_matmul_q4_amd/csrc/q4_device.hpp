@@ -9,18 +9,21 @@
 // kernels summed in different orders and dequantized at different times, so
 // a batching decision changed the numbers written to the KV cache.
 //
-// The order (version 3), for output (m, n), K = 32 * nb:
+// The order (version 4), for output (m, n), K = 32 * nb:
 //   quads:    G = ceil(nb / 4) groups of 4 blocks; the last may be short.
 //   segments: S = min(16, 2^floor(log2 G)); segment j covers quads
 //             [floor(j G / S), floor((j+1) G / S)), i.e. blocks
 //             [4 floor(j G / S), min(nb, 4 floor((j+1) G / S))).
-//   block dot s_b, one v_mfma_f32_16x16x32_{bf16,f16} (C = 0) per product
-//             with A row = x[m][32b .. 32b+31] in natural k order:
-//             fp16 x: s_b = D, B column = q[n][32b+k] - 8 (exact in fp16),
-//               so every product is exact and a zero weight adds exactly 0;
-//             bf16 x: s_b = fl(D - E), D with B column = 16 + q[n][32b+k],
-//               E with every B entry = 24 (both exact in bf16; E depends on
-//               x only); a block of all-8 codes gives D = E and s_b = 0
+//   block dot s_b, v_mfma_f32_16x16x32_{bf16,f16} with A row =
+//             x[m][32b .. 32b+31] in natural k order:
+//             fp16 x: s_b = MFMA(A, B, C = 0), B column = q[n][32b+k] - 8
+//               (exact in fp16), so every product is exact and a zero
+//               weight adds exactly 0;
+//             bf16 x: the correction C_b = MFMA(A, -24, C = 0) (every B
+//               entry -24; depends on x only), then s_b = MFMA(A, B, C =
+//               C_b) with B column = 16 + q[n][32b+k] (both operands exact
+//               in bf16): the matrix core adds the correction to the sum of
+//               the products itself.  A block of all-8 codes gives s_b = 0
 //               exactly.  (bf16 has no packed add on this target, so an
 //               exact q - 8 operand would cost about three times the
 //               dequantization work; the offset 16 keeps the cancellation
@@ -70,9 +73,9 @@ constexpr uint32_t kF16MaskHi = 0x00F000F0u;   // codes at bits 4..7 of each hal
 constexpr uint32_t kF16Bias = 0xE408E408u;     // -1032, -1032 (binary16)
 constexpr uint32_t kF16Sixteenth = 0x2C002C00u;  // 1/16, 1/16
 constexpr uint32_t kF16Bias16 = 0xD480D480u;   // -72, -72
-// B operand of the bf16 correction dot E: 24 in every entry.
-constexpr uint32_t kBf16Offset = 0x41C041C0u;
-// Whether the block dot carries the correction E (bf16) or is exact (fp16).
+// B operand of the bf16 correction dot: -24 in every entry.
+constexpr uint32_t kBf16Offset = 0xC1C0C1C0u;
+// Whether the block dot carries the correction (bf16) or is exact (fp16).
 template <bool BF16>
 constexpr bool kCorrected = BF16;
 
@@ -82,7 +85,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // the fp16 biases in scalar registers, the magic and 1/16 in vector ones (one
 // scalar operand per instruction on this target; three-operand instructions
 // take no literal).  The empty statements emit no instructions.  The bf16
-// correction's B operand (24 everywhere) is built once the same way, so the
+// correction's B operand (-24 everywhere) is built once the same way, so the
 // compiler keeps it in four registers instead of rebuilding it for every
 // block dot.
 template <bool BF16>
@@ -160,31 +163,52 @@ __device__ __forceinline__ f32x4 blockdot(u32x4 a, u32x4 b)
                                                       __builtin_bit_cast(f16x8, b), zero, 0, 0, 0);
 }
 
+// The same with the accumulator input C.
+template <bool BF16>
+__device__ __forceinline__ f32x4 blockdot_acc(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// The block's correction C_b = MFMA(A, -24) (bf16; x only), or zero (fp16:
+// unused).
+template <bool BF16>
+__device__ __forceinline__ f32x4 correction(u32x4 a, const Dequant<BF16> &dq)
+{
+    if constexpr (kCorrected<BF16>)
+        return blockdot<BF16>(a, dq.offset);
+    else
+        return (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// The block dot s_b with the operand b dequantized: MFMA(A, b, C = C_b)
+// (bf16) or MFMA(A, b, C = 0) (fp16).
+template <bool BF16>
+__device__ __forceinline__ f32x4 block_dot(u32x4 a, u32x4 b, f32x4 cb)
+{
+    if constexpr (kCorrected<BF16>)
+        return blockdot_acc<BF16>(a, b, cb);
+    else
+        return blockdot<BF16>(a, b);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// The block dot's value from the matrix-core results: fl(D - E) (bf16; the
-// difference rounds first: -ffp-contract=off keeps it a separate step) or
-// D itself (fp16, exact operands).
-template <bool BF16>
-__device__ __forceinline__ float block_value(float D, float E)
-{
-    if constexpr (kCorrected<BF16>)
-        return D - E;
-    else
-        return D;
-}
-
 // p = fmaf(d, s_b, p) for the four accumulator rows a lane holds.
-template <bool BF16>
-__device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 D, f32x4 E)
+__device__ __forceinline__ void scale_accumulate(f32x4 &p, float d, f32x4 s)
 {
-    p.x = __builtin_fmaf(d, block_value<BF16>(D.x, E.x), p.x);
-    p.y = __builtin_fmaf(d, block_value<BF16>(D.y, E.y), p.y);
-    p.z = __builtin_fmaf(d, block_value<BF16>(D.z, E.z), p.z);
-    p.w = __builtin_fmaf(d, block_value<BF16>(D.w, E.w), p.w);
+    p.x = __builtin_fmaf(d, s.x, p.x);
+    p.y = __builtin_fmaf(d, s.y, p.y);
+    p.z = __builtin_fmaf(d, s.z, p.z);
+    p.w = __builtin_fmaf(d, s.w, p.w);
 }
 
 // Streaming form of the pairwise tree for one wave that owns an aligned run

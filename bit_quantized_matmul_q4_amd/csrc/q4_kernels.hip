@@ -90,22 +90,20 @@ __device__ __forceinline__ void gemv_quad(const GemvStage &st, const u32x4 (&xa)
     const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
     const uint32_t h[4] = {st.s.x & 0xFFFFu, st.s.x >> 16, st.s.y & 0xFFFFu, st.s.y >> 16};
     // the block dots first, so their matrix-core latencies overlap
-    f32x4 D[4], E[4];
+    f32x4 C[4], D[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        D[i] = blockdot<BF16>(xa[i], dq(w[i]));
-        if constexpr (kCorrected<BF16>)
-            E[i] = blockdot<BF16>(xa[i], dq.offset);
-        else
-            E[i] = D[i];  // unused
-    }
+    for (int i = 0; i < 4; ++i)
+        C[i] = correction<BF16>(xa[i], dq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        D[i] = block_dot<BF16>(xa[i], dq(w[i]), C[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (!SHORT || i < nq) {
             const float d = half_bits_to_float(h[i]);
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                p[r] = __builtin_fmaf(d, block_value<BF16>(D[i][r], E[i][r]), p[r]);
+                p[r] = __builtin_fmaf(d, D[i][r], p[r]);
         }
     }
 }
@@ -119,37 +117,34 @@ __device__ __forceinline__ void gemv_block_values(const GemvStage &st, const u32
     const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x4 D = blockdot<BF16>(xa[i], dq(w[i]));
-        f32x4 E = D;
-        if constexpr (kCorrected<BF16>)
-            E = blockdot<BF16>(xa[i], dq.offset);
+        const f32x4 D = block_dot<BF16>(xa[i], dq(w[i]), correction<BF16>(xa[i], dq));
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            bv[i][r] = block_value<BF16>(D[r], E[r]);
+            bv[i][r] = D[r];
     }
 }
 
-// gemv_quad with the quad's correction dots already computed (Eq[i][r]: the
-// value E of block i for accumulator row r), for waves that hold their x
-// for many tiles: E depends on x only, so the same instruction on the same
-// operands gives the same bits wherever it runs.
+// gemv_quad with the quad's corrections already computed (Cq[i]: block
+// i's), for waves that hold their x for many tiles: the correction depends
+// on x only, so the same instruction on the same operands gives the same
+// bits wherever it runs.
 template <bool BF16, int R, bool SHORT>
-__device__ __forceinline__ void gemv_quad_pre(const GemvStage &st, const u32x4 (&xa)[4], const float (&Eq)[4][R],
-                                              int nq, const Dequant<BF16> &dq, float (&p)[R])
+__device__ __forceinline__ void gemv_quad_pre(const GemvStage &st, const u32x4 (&xa)[4], const f32x4 (&Cq)[4], int nq,
+                                              const Dequant<BF16> &dq, float (&p)[R])
 {
     const uint32_t w[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
     const uint32_t h[4] = {st.s.x & 0xFFFFu, st.s.x >> 16, st.s.y & 0xFFFFu, st.s.y >> 16};
     f32x4 D[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        D[i] = blockdot<BF16>(xa[i], dq(w[i]));
+        D[i] = block_dot<BF16>(xa[i], dq(w[i]), Cq[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (!SHORT || i < nq) {
             const float d = half_bits_to_float(h[i]);
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                p[r] = __builtin_fmaf(d, block_value<BF16>(D[i][r], Eq[i][r]), p[r]);
+                p[r] = __builtin_fmaf(d, D[i][r], p[r]);
         }
     }
 }
@@ -940,20 +935,16 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     }
 
     const Dequant<BF16> dq;
-    // bf16: the segment's correction dots once, for all the wave's tiles,
-    // where the registers allow (LQ 4 R values a lane)
-    constexpr bool HOIST = kCorrected<BF16> && LQ * 4 * R <= 16;
-    float Eh[LQ][4][R];
+    // bf16: the segment's corrections once, for all the wave's tiles, where
+    // the registers allow (4 LQ accumulator inputs, 16 LQ a lane)
+    constexpr bool HOIST = kCorrected<BF16> && LQ <= 2 && R <= 2;
+    f32x4 Ch[HOIST ? LQ : 1][4];
     if constexpr (HOIST) {
 #pragma unroll
         for (int q = 0; q < LQ; ++q)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const f32x4 e = blockdot<BF16>(xs[q][b], dq.offset);
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    Eh[q][b][r] = e[r];
-            }
+            for (int b = 0; b < 4; ++b)
+                Ch[q][b] = correction<BF16>(xs[q][b], dq);
     }
     float p[R];
 #pragma unroll
@@ -972,7 +963,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
                 st.s.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sg_cur.y);
             }
             if constexpr (HOIST)
-                gemv_quad_pre<BF16, R, SHORT>(st, xs[q], Eh[q], nq, dq, p);
+                gemv_quad_pre<BF16, R, SHORT>(st, xs[q], Ch[HOIST ? q : 0], nq, dq, p);
             else
                 gemv_quad<BF16, R, SHORT>(st, xs[q], nq, dq, p);
         }
@@ -1126,7 +1117,7 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
     };
     if constexpr (RT == 1) {
         u32x4 A[4], B[4];
-        f32x4 E[4], Dm[4];
+        f32x4 C[4], Dm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             A[i] = *(const u32x4 *)(stg + gemm_ws_a_offset(0, i, lane));
@@ -1135,18 +1126,14 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
             B[i] = dq(wd[i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if constexpr (kCorrected<BF16>)
-                E[i] = blockdot<BF16>(A[i], dq.offset);
+            C[i] = correction<BF16>(A[i], dq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Dm[i] = blockdot<BF16>(A[i], B[i]);
-            if constexpr (!kCorrected<BF16>)
-                E[i] = Dm[i];  // unused
-        }
+        for (int i = 0; i < 4; ++i)
+            Dm[i] = block_dot<BF16>(A[i], B[i], C[i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (!SHORT || i < nq)  // blocks past a short last quad: not accumulated
-                scale_accumulate<BF16>(p[0], scale(i), Dm[i], E[i]);
+                scale_accumulate(p[0], scale(i), Dm[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1157,21 +1144,17 @@ __device__ __forceinline__ void gemm_ws_quad(u32x4 w, u32x2 s, const uint8_t *st
                 for (int rt = 0; rt < RT; ++rt)
                     A[rt] = *(const u32x4 *)(stg + gemm_ws_a_offset(rt, i, lane));
                 // the block dots first, so they overlap in the matrix pipe
-                f32x4 E[RT], Dm[RT];
+                f32x4 C[RT], Dm[RT];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    if constexpr (kCorrected<BF16>)
-                        E[rt] = blockdot<BF16>(A[rt], dq.offset);
+                    C[rt] = correction<BF16>(A[rt], dq);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    Dm[rt] = blockdot<BF16>(A[rt], B);
-                    if constexpr (!kCorrected<BF16>)
-                        E[rt] = Dm[rt];  // unused
-                }
+                for (int rt = 0; rt < RT; ++rt)
+                    Dm[rt] = block_dot<BF16>(A[rt], B, C[rt]);
                 const float dsc = scale(i);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    scale_accumulate<BF16>(p[rt], dsc, Dm[rt], E[rt]);
+                    scale_accumulate(p[rt], dsc, Dm[rt]);
             }
         }
     }

@@ -38,21 +38,29 @@ __global__ __launch_bounds__(256) void probe_dequant(const uint32_t *w, q4::u32x
         out[i] = q4::Dequant<BF16>()(w[i]);
 }
 
+// One MFMA per wave with the accumulator input c: d = MFMA(a, b, C = c).
+template <bool BF16>
+__global__ __launch_bounds__(64) void probe_mfma_acc(const q4::u32x4 *a, const q4::u32x4 *b, const q4::f32x4 *c,
+                                                     q4::f32x4 *d)
+{
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    d[i] = q4::blockdot_acc<BF16>(a[i], b[i], c[i]);
+}
+
 // The block dot of the order as the kernels run it: for lane data a (A
-// operand) and one packed code word w per lane, D = MFMA(a, dequant(w)) and
-// (bf16) E = MFMA(a, 24) or (fp16, no correction) E = 0; both are returned,
-// [waves][64][4] each.
+// operand) and one packed code word w per lane, the correction C = MFMA(a,
+// -24) (bf16) or 0 (fp16) and the block dot D = MFMA(a, dequant(w), C = C)
+// (bf16) or MFMA(a, dequant(w)) (fp16); both are returned, [waves][64][4]
+// each.
 template <bool BF16>
 __global__ __launch_bounds__(64) void probe_q4dot(const q4::u32x4 *a, const uint32_t *w, q4::f32x4 *d,
                                                   q4::f32x4 *e)
 {
     const int i = blockIdx.x * 64 + threadIdx.x;
     const q4::Dequant<BF16> dq;
-    d[i] = q4::blockdot<BF16>(a[i], dq(w[i]));
-    if constexpr (q4::kCorrected<BF16>)
-        e[i] = q4::blockdot<BF16>(a[i], dq.offset);
-    else
-        e[i] = (q4::f32x4){0.f, 0.f, 0.f, 0.f};
+    const q4::f32x4 c = q4::correction<BF16>(a[i], dq);
+    d[i] = q4::block_dot<BF16>(a[i], dq(w[i]), c);
+    e[i] = c;
 }
 
 // fmaf(d, s, +0) on the VALU, for the single-rounding check of the scale step.
@@ -176,6 +184,19 @@ int q4probe_read(const void *src, size_t bytes, void *sink, int blocks, void *st
         return -1;
     hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(512), 0, (hipStream_t)stream, (const q4::u32x4 *)src,
                        bytes / 16, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int q4probe_mfma_acc(const void *a, const void *b, const void *c, void *d, int waves, int bf16, void *stream)
+{
+    if (!a || !b || !c || !d || waves < 1)
+        return -1;
+    if (bf16)
+        hipLaunchKernelGGL(probe_mfma_acc<true>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const q4::u32x4 *)b, (const q4::f32x4 *)c, (q4::f32x4 *)d);
+    else
+        hipLaunchKernelGGL(probe_mfma_acc<false>, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                           (const q4::u32x4 *)a, (const q4::u32x4 *)b, (const q4::f32x4 *)c, (q4::f32x4 *)d);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

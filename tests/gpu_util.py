@@ -81,6 +81,7 @@ class Probe:
         self.lib = ctypes.CDLL(build.PROBE_LIB)
         vp, i = ctypes.c_void_p, ctypes.c_int
         self.lib.q4probe_mfma.argtypes = [vp, vp, vp, i, i, vp]
+        self.lib.q4probe_mfma_acc.argtypes = [vp, vp, vp, vp, i, i, vp]
         self.lib.q4probe_dequant.argtypes = [vp, vp, i, i, vp]
         self.lib.q4probe_fma0.argtypes = [vp, vp, vp, i, vp]
         self.lib.q4probe_q4dot.argtypes = [vp, vp, vp, vp, i, i, vp]
@@ -97,6 +98,19 @@ class Probe:
         torch.cuda.synchronize()
         return d.cpu().numpy()
 
+    def mfma_acc(self, a_lanes: np.ndarray, b_lanes: np.ndarray, c_lanes: np.ndarray, bf16: bool) -> np.ndarray:
+        """The same with the accumulator input c_lanes (float32 [waves, 64, 4])."""
+        waves = a_lanes.shape[0]
+        a = torch.from_numpy(np.ascontiguousarray(a_lanes, np.uint16).view(np.int16)).to(DEV)
+        b = torch.from_numpy(np.ascontiguousarray(b_lanes, np.uint16).view(np.int16)).to(DEV)
+        c = torch.from_numpy(np.ascontiguousarray(c_lanes, np.float32)).to(DEV)
+        d = torch.empty((waves, 64, 4), dtype=torch.float32, device=DEV)
+        rc = self.lib.q4probe_mfma_acc(a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(), waves, int(bf16),
+                                       torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        return d.cpu().numpy()
+
     def dequant(self, words: np.ndarray, bf16: bool) -> np.ndarray:
         """uint32 [n] -> uint16 [n, 8] operand values."""
         n = words.shape[0]
@@ -109,8 +123,8 @@ class Probe:
         return out.cpu().numpy().view(np.uint16).reshape(n, 8)
 
     def q4dot(self, a_lanes: np.ndarray, words: np.ndarray, bf16: bool):
-        """a_lanes uint16 [waves, 64, 8], words uint32 [waves, 64] -> (D, E)
-        float32 [waves, 64, 4] each: the block dot and its correction."""
+        """a_lanes uint16 [waves, 64, 8], words uint32 [waves, 64] -> (D, C)
+        float32 [waves, 64, 4] each: the block dot and its correction input."""
         waves = a_lanes.shape[0]
         a = torch.from_numpy(np.ascontiguousarray(a_lanes, np.uint16).view(np.int16)).to(DEV)
         w = torch.from_numpy(np.ascontiguousarray(words, np.uint32).view(np.int32)).to(DEV)

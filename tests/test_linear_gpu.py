@@ -171,10 +171,11 @@ def test_f16_sparse_deviation_worst_regime(kernel, K):
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 @pytest.mark.parametrize("K", [32, 896, 3584])
 def test_bf16_sparse_deviation(kernel, K):
-    """bf16 with one non-zero weight per block.  The bf16 block dot is
-    fl(D - E) with operands 16 + q and 24, so its error is bounded by the
-    block's sum of |x| rather than by A: |s_b - exact| <= 33 u (31 + 24)
-    sum|x| + u |exact|.  Checked output by output against the oracle with
+    """bf16 with one non-zero weight per block.  The bf16 block dot is the
+    MFMA of the operand 16 + q with the correction MFMA(x, -24) as its
+    accumulator input, so its error is bounded by the block's sum of |x|
+    rather than by A: |s_b - exact| <= 33 u (31 + 24 (2 + 33 u)) sum|x|.
+    Checked output by output against the oracle with
     that bound carried through the scale and accumulation steps.  Against
     2e-3 of A: integer activations up to 4000 (every D and E exact), and
     N(0, 1) activations from K = 896 on (at K = 32 a block whose only
@@ -201,7 +202,7 @@ def test_bf16_sparse_deviation(kernel, K):
         # the absolute bound, from the blocks' sums of |x| and the scales
         xa = np.abs((np.asarray(x, np.uint32) << 16).view(np.float32).astype(np.float64))
         xsum = xa.reshape(M, K // 32, 32).sum(axis=2)  # [M, nb]
-        blk = (33 * u * 55.0) * xsum @ d.T            # sum_b d_b (block-dot bound)
+        blk = (33 * u * (31.0 + 24.0 * (2.0 + 33 * u))) * xsum @ d.T  # sum_b d_b (block-dot bound)
         bound = blk + F16_ORDER_BOUND * a_ref           # plus the accumulation's
         assert np.all(np.abs(y.astype(np.float64) - y_ref) <= bound), name
 

@@ -8,10 +8,11 @@
 * exactness when every partial sum is representable;
 * the nibble dequantization gives the operand exactly for every code at
   every position of a packed word: 16 + q in bf16, q - 8 in fp16;
-* the bf16 corrected block dot: D = MFMA(x, 16 + q) is the plain MFMA of
-  the dequantized operand, E = MFMA(x, 24) is the same for every column,
-  D == E for a block of all-8 codes, and fl(D - E) is within the fp32
-  accumulation bound of the exact sum of x (q - 8);
+* the bf16 corrected block dot: the correction C = MFMA(x, -24) is the same
+  for every column and the exact negation of MFMA(x, 24); the block dot is
+  the MFMA of the dequantized operand 16 + q with C as its accumulator
+  input, and is within the fp32 accumulation bound of the exact sum of
+  x (q - 8);
 * the fp16 block dot D = MFMA(x, q - 8) is within the fp32 accumulation
   bound of the exact sum relative to sum |x (q - 8)| (zero weights add
   exactly nothing), and a block with one non-zero weight is exact;
@@ -172,25 +173,29 @@ def test_corrected_block_dot_bf16(probe):
     q = rng.integers(0, 16, size=(w, 32, 16)).astype(np.uint32)
     q[:16] = 8  # all-8 blocks
     a4, b4 = to_lanes(A, operand_bits(q, True))
-    D, E = probe.q4dot(a4, lane_words(q), True)
-    # D is the plain MFMA of the dequantized operand
-    assert np.array_equal(D.view(np.uint32), probe.mfma(a4, b4, True).view(np.uint32))
-    Dm, Em = from_lanes(D), from_lanes(E)
-    # E depends on the row only, and is the MFMA against 24 everywhere
-    assert np.array_equal(Em.view(np.uint32), np.repeat(Em[:, :, :1], 16, axis=2).view(np.uint32))
+    D, C = probe.q4dot(a4, lane_words(q), True)
+    Dm, Cm = from_lanes(D), from_lanes(C)
+    # the correction depends on the row only: the MFMA against -24
+    # everywhere, and bit for bit the negation of the MFMA against 24
+    assert np.array_equal(Cm.view(np.uint32), np.repeat(Cm[:, :, :1], 16, axis=2).view(np.uint32))
+    _, bm24 = to_lanes(A, np.full((w, 32, 16), enc(np.array([-24.0]), True)[0], np.uint16))
+    assert np.array_equal(C.view(np.uint32), probe.mfma(a4, bm24, True).view(np.uint32))
     _, b24 = to_lanes(A, np.full((w, 32, 16), enc(np.array([24.0]), True)[0], np.uint16))
-    assert np.array_equal(E.view(np.uint32), probe.mfma(a4, b24, True).view(np.uint32))
-    # a block of all-8 codes: D == E, so the block dot is exactly zero
-    assert np.array_equal(Dm[:16].view(np.uint32), Em[:16].view(np.uint32))
-    # fl(D - E) against the exact sum: each of D and E is a sum of 32 exact
-    # products (operands at most 31 and 24), so within 33 u of their sums of
-    # magnitudes, plus the subtraction's own rounding
+    assert np.array_equal(C.view(np.uint32), (-probe.mfma(a4, b24, True)).view(np.uint32))
+    # the block dot is the MFMA of the dequantized operand with the
+    # correction as accumulator input
+    assert np.array_equal(D.view(np.uint32), probe.mfma_acc(a4, b4, C, True).view(np.uint32))
+    # against the exact sum: the block dot sums 32 exact products (operands
+    # at most 31) and C, the correction 32 exact products (24), each within
+    # 33 u of its sum of magnitudes, |C| at most 24 (1 + 33 u) sum|x|
     xd = dec(A, True)
-    s = (Dm - Em).astype(np.float32).astype(np.float64)
+    s = Dm.astype(np.float64)
     exact = np.einsum("wmk,wkn->wmn", xd, q.astype(np.float64) - 8.0)
     u = 2.0 ** -24
-    bound = 33 * u * (31.0 + 24.0) * np.abs(xd).sum(axis=2)[:, :, None] + u * np.abs(exact)
+    bound = 33 * u * (31.0 + 24.0 * (2.0 + 33 * u)) * np.abs(xd).sum(axis=2)[:, :, None]
     assert np.all(np.abs(s - exact) <= bound)
+    # a block of all-8 codes: the exact value is 0, the result within the bound
+    assert np.all(np.abs(s[:16]) <= bound[:16])
 
 
 def test_exact_operand_block_dot_f16(probe):
