@@ -62,6 +62,9 @@ SHAPES = [
     (6, 300, 3616, True), (8, 40, 896, False),
     (3, 4100, 3584, True), (2, 4100, 4128, True), (7, 6150, 4864, False),
     (3, 65552, 1024, True), (6, 65552, 1024, False),
+    # one row: the prefill's x first (per-wave slots; a run the prefill
+    # holds whole, and a long one)
+    (1, 512, 3584, True), (1, 130, 18944, True),
 ]
 
 
@@ -82,6 +85,9 @@ SEG_SHAPES = [
     (1, 4100, 2048, True), (2, 4112, 2080, False), (3, 8210, 3584, True), (2, 8210, 4128, True),
     (9, 4100, 2048, False), (1, 8210, 2048, True), (8, 4352, 3584, True), (16, 4112, 3584, True),
     (13, 8210, 2080, False),
+    # up to four rows x staged by the workgroup, scales in groups, a short
+    # last quad
+    (2, 8210, 2080, True), (4, 12000, 3616, False),
 ]
 
 
