@@ -766,8 +766,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 //  * up to four rows (R = 1) the workgroup stages x in LDS, one 16-byte load
 //    a thread and 16 KB (waves past x's bytes issue none), and each wave
 //    reads its A operands from there (lanes of row slots past the batch read
-//    nothing); with more rows each wave loads its own, four 16-byte loads a
-//    quad (gate at one row 10.1 -> 9.7 us, gate|up 17.6 -> 16.6 us);
+//    nothing) (gate at one row 10.1 -> 9.7 us, gate|up 17.6 -> 16.6 us);
+//    from 5 to 8 rows with segments of up to 2 quads each wave loads its
+//    segment's rows in row order, every lane 16 useful bytes, and forms its
+//    A operands through its own LDS slot (gate at 5 rows 10.3 -> 9.8 us,
+//    gate|up 17.4 -> 16.7 us); otherwise each wave loads them directly,
+//    four 16-byte loads a quad;
 //  * with whole ring rounds of four stages (LQ <= 2, R <= 2) the scales come
 //    in groups of four positions, one 8-byte load a lane for the group: the
 //    lanes of row g load position g's column scales and each position's reach
@@ -779,7 +783,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 // min(M, 16), dynamic LDS: roots [NB][TC][16 seg][MR][16] floats (NB = 1
 // if tpw <= TC: one combine after the last tile; else 2, double-buffered),
 // then outputs [tpw][MR][16] floats, then (R = 1) x, M rows of 2 K bytes
-// and 256 bytes of slack (seg_lds_bytes).
+// and 256 bytes of slack, or (R = 2, LQ <= 2) 16 per-wave slots of 8 rows of
+// 256 LQ + 16 bytes (seg_lds_bytes).
 // TC: tiles per combine.  Measured on MI355X: with up to 8 tiles per
 // workgroup one combine at the end is fastest (gate at one row 10.7 ->
 // 10.4 us, at 9 rows 13.2 -> 12.4 us); with more tiles (gate|up, the LM
@@ -817,7 +822,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     const int MR = min(M, 16);
     float *roots = seg_lds;                                         // [NB][TC][16 seg][MR][16]
     float *ystage = seg_lds + seg_nbuf(TC, tpw) * TC * 16 * MR * 16;  // [tpw][MR][16]
-    uint8_t *x_lds = (uint8_t *)(ystage + tpw * MR * 16);              // R = 1: [mrows][2 K bytes]
+    uint8_t *x_lds = (uint8_t *)(ystage + tpw * MR * 16);              // x staged or the x slots
 
     const MatrixSel sel = select_matrix(items);
     const uint8_t *__restrict__ wq = sel.wq;
@@ -848,7 +853,29 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     const uint32_t x_wave = (uint32_t)(threadIdx.x & ~63u) * 16u;  // the wave's first chunk byte
     u32x4 xs[LQ][4];
     u32x4 xv[XV];
-    if constexpr (XLDS) {
+    // 5 to 8 rows, segments of up to 2 quads: the wave loads its segment's
+    // rows in row order (every lane 16 useful bytes: 2 LQ loads instead of
+    // 4 LQ) and turns them into A operands through its own LDS slot
+    constexpr bool XWS = R == 2 && LQ <= 2;
+    constexpr uint32_t XS_ROW = 256u * LQ + 16u;  // a row in the slot (padded)
+    constexpr int XN = 2 * LQ;                    // 8 rows x 16 LQ chunks / 64 lanes
+    u32x4 xw[XN];
+    auto xw_chunk = [&](int u, uint32_t &row, uint32_t &ch) {
+        const uint32_t id = 64u * (uint32_t)u + (uint32_t)lane;
+        row = id / (16u * LQ);
+        ch = id % (16u * LQ);
+    };
+    if constexpr (XWS) {
+#pragma unroll
+        for (int u = 0; u < XN; ++u) {
+            uint32_t row, ch;
+            xw_chunk(u, row, ch);
+            const uint32_t qq = min((int)(ch >> 4), len - 1);
+            const uint32_t off = (int)row < mrows ? row * (uint32_t)K * 2u + 256u * (qs + qq) + 16u * (ch & 15u)
+                                                  : x_bytes;
+            xw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        }
+    } else if constexpr (XLDS) {
 #pragma unroll
         for (int u = 0; u < XV; ++u)
             if (x_wave + 16384u * u < x_bytes)  // wave-uniform: whole waves past x issue nothing
@@ -910,6 +937,27 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
     }
     // (no wait for the whole prefill here: the first stage's wait covers x,
     // loaded before it; measured: gate 10.3 -> 10.1 us)
+    if constexpr (XWS) {
+        uint8_t *const slot = x_lds + (uint32_t)j * (8u * XS_ROW);
+#pragma unroll
+        for (int u = 0; u < XN; ++u) {
+            uint32_t row, ch;
+            xw_chunk(u, row, ch);
+            *(u32x4 *)(slot + row * XS_ROW + 16u * ch) = xw[u];
+        }
+        // (the wave's own slot: its LDS operations complete in order)
+#pragma unroll
+        for (int q = 0; q < LQ; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                xs[q][b] = u32x4{0u, 0u, 0u, 0u};
+        if (xr < mrows)
+#pragma unroll
+            for (int q = 0; q < LQ; ++q)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    xs[q][b] = *(const u32x4 *)(slot + (uint32_t)xr * XS_ROW + 256u * q + 64u * b + 16u * g);
+    }
     if constexpr (XLDS) {
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
@@ -1850,8 +1898,13 @@ static size_t seg_lds_bytes(int M, int K, int tpw)
 {
     const int MR = M < 16 ? M : 16;
     const int tc = seg_tc(M, tpw);
-    // up to four rows x is staged too (2 K bytes a row and 256 of slack)
-    const size_t x = M <= 4 ? (size_t)M * K * 2 + 256 : 0;
+    // up to four rows x is staged too (2 K bytes a row and 256 of slack);
+    // from 5 to 8 rows with segments of up to 2 quads each wave has a slot of
+    // 8 rows of 256 LQ + 16 bytes
+    const Plan plan = make_plan(K);
+    const int LQ = (plan.G + 15) / 16;
+    const size_t x = M <= 4 ? (size_t)M * K * 2 + 256
+                     : (M <= 8 && plan.S == 16 && LQ <= 2) ? (size_t)16 * 8 * (256 * LQ + 16) : 0;
     return (size_t)64 * MR * (seg_nbuf(tc, tpw) * tc * 16 + tpw) + x;
 }
 
