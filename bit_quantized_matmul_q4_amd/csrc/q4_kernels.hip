@@ -1121,7 +1121,7 @@ __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__
 // rows into registers two quads ahead and written to a two-stage LDS ring
 // one quad ahead; one barrier per quad publishes a stage.  Per block a wave
 // dequantizes its B operand once for its RT row tiles and runs RT block
-// dots (bf16: 2 RT, D and the correction E of each row tile).
+// dots (bf16: 2 RT, the correction of each row tile and its block dot).
 //
 // The grid is one-dimensional over (column unit, row unit) and K-groups in y:
 // workgroup id -> column unit 8 (id / 8 nru) + id % 8, row unit (id / 8) %
