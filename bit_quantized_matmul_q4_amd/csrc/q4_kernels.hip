@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "q4_device.hpp"
 #include "q4_launch.hpp"
@@ -367,10 +368,14 @@ __device__ __forceinline__ MatrixSel select_matrix(const MatrixItems<NM> items)
 //    run L + L - 1) of tile slot `slot`; each tile's W run roots meet in LDS
 //    for the top of the pairwise tree.
 //  XM (see XM_RING, XM_LDS, XM_WAVE): where the A operands come from.
+//  XF: 0, x loaded with each stage's codes; 1 (one row), x first in the
+//    prefill; 2 (bf16 split form, up to 8 rows, every run held whole by the
+//    prefill), x first and the corrections of all stages computed while the
+//    codes are still in flight.
 // Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
 // (XM_LDS) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of
 // slack, or (XM_WAVE) one slot of 4 R rows of XW_ROW bytes per wave.
-template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM, bool XF>
+template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM, int XF>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x, MatrixItems<NM> items,
                                                               int M, int K, Plan plan, int L, int tps)
 {
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     GemvStream in;
     in.w = buffer_rsrc(wq + ((size_t)min(t0, n16 - 1) * G + q0) * 1024, (uint32_t)total * 1024u);
     in.s = buffer_rsrc(scales + ((size_t)min(t0, n16 - 1) * G + q0) * 64, (uint32_t)total * 128u);
-    if constexpr (XF) {
+    if constexpr (XF != 0) {
         // x's loads stay where they are written (the compiler may otherwise
         // move loads of a read-only argument down to their first use, here
         // behind the wait for the prefill)
@@ -515,12 +520,13 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         sg_next = load_group();
         issue_fence();
     }
-    // XF (one row): the prefill's x first, then its codes.  Otherwise the x
-    // of each prefill stage is written with its codes but the compiler issues
-    // it after the wait below (see XF), one round trip to cache later.
-    // Measured on MI355X: at one row x first is faster (down_proj 10.8 ->
-    // 9.8 us), from two rows x after the codes (k_proj at 8 rows 5.2 -> 4.7 us).
-    if constexpr (XF) {
+    // XF != 0: the prefill's x first, then its codes.  Otherwise the x of
+    // each prefill stage is written with its codes but the compiler issues it
+    // after the wait below (see XF), one round trip to cache later.  Measured
+    // on MI355X: at one row x first is faster (down_proj 10.8 -> 9.8 us);
+    // from two rows, without XF = 2's corrections ahead, x after the codes
+    // (k_proj at 8 rows 5.2 -> 4.7 us).
+    if constexpr (XF != 0) {
         int qx = ql, lx = left;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) {  // in stage order (see the refill below)
-        gemv_load<XM, R, !SG, !XF>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
+        gemv_load<XM, R, !SG, XF == 0>(ring[d], in, left > 0 ? 256u * ql : x_bytes);
         ql = ql + 1 == q1 ? q0 : ql + 1;
         --left;
         issue_fence();
@@ -546,12 +552,17 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         }
         __syncthreads();
     }
+    // A split-form run that the prefill holds whole (total <= D: q, k and v
+    // of the 7B set) is computed from the ring without a loop (below).
+    const bool whole = SPLIT && !XL && (R == 1 || XF == 2) && total <= D;
     // The compiler may reorder the prefill's loads (it clusters loads from
     // one base).  Waiting for all of them here costs little (they were issued
     // together and the first compute needs the first of them) and keeps that
     // order from pessimising every wait of the loop, whose header merges the
-    // prefill's pending loads with the refills'.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // prefill's pending loads with the refills'.  (XF = 2: the compiler's
+    // own waits, x before the codes.)
+    if (!(XF == 2 && whole))
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     const Dequant<BF16> dq;
     // accumulators: the R rows a lane can hold (batch rows g + 4 r, r < R)
@@ -594,15 +605,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         }
         qc = qn;
     };
-    // A split-form run that the prefill holds whole (total <= D: q, k and v
-    // of the 7B set): every stage's A operands and block dots first, so that
-    // the stages' LDS and matrix-core latencies overlap (such runs often have
-    // a SIMD to themselves), then the scale-accumulates in order.  Measured
-    // on MI355X: a stage costs ~0.25 us of latency one after the other; up to
-    // 4 rows this takes q_proj 4.9 -> 4.6 us, k_proj 4.3 -> 4.0 us and 896 x
-    // 896 3.3 -> 3.2 us (at 8 rows the registers it needs cost more than it
-    // saves).
-    const bool whole = SPLIT && !XL && R == 1 && total <= D;
+    // A run held whole: every stage's A operands and block dots first, so
+    // that the stages' LDS and matrix-core latencies overlap (such runs often
+    // have a SIMD to themselves), then the scale-accumulates in order.
+    // Measured on MI355X: a stage costs ~0.25 us of latency one after the
+    // other; up to 4 rows this takes q_proj 4.9 -> 4.6 us, k_proj 4.3 -> 4.0
+    // us and 896 x 896 3.3 -> 3.2 us (at 8 rows the registers it needs cost
+    // more than it saves, without XF = 2).  XF = 2 loads x first and computes
+    // the corrections before the codes arrive, up to 8 rows (q_proj at 1 / 4
+    // / 8 rows 4.55 / 4.64 / 5.32 -> 4.34 / 4.41 / 4.85 us, k_proj 3.92 /
+    // 4.17 / 4.65 -> 3.79 / 3.99 / 4.46 us); it has its own instantiation, as
+    // the registers it holds (the A operands and corrections of all stages)
+    // slow the longer runs of down_proj by 4%.
     if (whole) {
         if constexpr (SG) {
             sg_cur = sg_next;
@@ -614,6 +628,43 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             }
         }
         float bv[D][4][R];
+        // XF = 2: all stages' corrections, then their block dots once the
+        // codes are there (guarded: only the stages the run holds)
+        auto ahead = [&](auto guarded) {
+            constexpr bool GD = decltype(guarded)::value;
+            u32x4 xa[D][4];
+            f32x4 C[D][4];
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (!GD || d < total) {
+                    if constexpr (XM == XM_WAVE)
+                        gemv_x_wave<R>(xa[d], ring[d], wput, xget);
+                    else if constexpr (XM == XM_QUAD)
+                        gemv_x_quad<R>(xa[d], ring[d]);
+                    else
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            xa[d][b] = ring[d].xa[b];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        C[d][b] = correction<BF16>(xa[d][b], dq);
+                }
+            }
+            issue_fence();
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (!GD || d < total) {
+                    const uint32_t w[4] = {ring[d].w.x, ring[d].w.y, ring[d].w.z, ring[d].w.w};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const f32x4 v = block_dot<BF16>(xa[d][b], dq(w[b]), C[d][b]);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            bv[d][b][r] = v[r];
+                    }
+                }
+            }
+        };
         auto stage_values = [&](int d) {
             u32x4 xa[4];
             if constexpr (XM == XM_WAVE)
@@ -629,7 +680,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         // (a run one stage short of the ring computes the spare stage on
         // zeros rather than branch around it: no branch splits the stages'
         // instructions, q_proj 4.73 -> 4.60 us)
-        if (total >= D - 1) {
+        if constexpr (XF == 2) {
+            if (total >= D - 1)
+                ahead(std::false_type{});
+            else
+                ahead(std::true_type{});
+        } else if (total >= D - 1) {
 #pragma unroll
             for (int d = 0; d < D; ++d)
                 stage_values(d);
@@ -794,12 +850,16 @@ __host__ __device__ inline int seg_tc(int M, int tpw) { return tpw <= 8 ? 8 : M 
 __host__ __device__ inline int seg_nbuf(int tc, int tpw) { return tpw <= tc ? 1 : 2; }
 // Ring depth of the segment form (a multiple of LQ).  Measured on MI355X:
 // 4 stages beat 6, 8 and 10 (a deep per-wave prefetch delays the data each
-// wave needs first and scatters the workgroup's accesses; 2 helps at one row
-// but loses on the widest matrices).
-template <int R, int LQ>
+// wave needs first and scatters the workgroup's accesses).  With 2-quad
+// segments, up to 8 tiles a workgroup (one combine) and up to 8 rows, 2
+// stages beat 4: 16 waves of a compute unit then keep ~36 KB in flight
+// instead of ~72 KB (gate_proj 18944 x 3584 at one row 9.29 -> 8.98 us, at
+// eight 9.87 -> 9.54 us; 32768 x 3584 14.4 -> 14.1 us), not from 9 rows on
+// (32768 x 3584 at 16 rows 18.1 -> 18.2 us) nor with more tiles.
+template <int R, int LQ, int TC>
 constexpr int seg_depth()
 {
-    return LQ == 3 ? 6 : 4;
+    return LQ == 3 ? 6 : LQ == 2 && TC == 8 && R <= 2 ? 2 : 4;
 }
 
 __device__ __forceinline__ void workgroup_barrier_lds()
@@ -816,7 +876,7 @@ template <bool BF16, int R, int LQ, bool SHORT, int TC, int NM>
 __global__ __launch_bounds__(1024) void q4_gemv_seg(const uint16_t *__restrict__ x, MatrixItems<NM> items, int M, int K,
                                                     Plan plan, int tpw)
 {
-    constexpr int D = seg_depth<R, LQ>();  // ring depth: a multiple of LQ
+    constexpr int D = seg_depth<R, LQ, TC>();  // ring depth: a multiple of LQ
     static_assert(D % LQ == 0, "ring positions must map to fixed quads");
     extern __shared__ __attribute__((aligned(16))) float seg_lds[];
     const int MR = min(M, 16);
@@ -1708,38 +1768,61 @@ static MatrixItems<NM> narrow_items(const MatrixItems<kGroupMax> &m)
     return r;
 }
 
+// Whether every run of the split form (L segments, S / L runs a tile) has
+// at most D quads, so that the prefill holds it whole.
+static bool split_runs_whole(const Plan &plan, int L, int D)
+{
+    for (int seg0 = 0; seg0 < plan.S; seg0 += L)
+        if ((((seg0 + L) * plan.G) >> plan.log2S) - ((seg0 * plan.G) >> plan.log2S) > D)
+            return false;
+    return true;
+}
+
 template <bool BF16, int R, int D, bool SPLIT, int XL, int NM>
 static void launch_gemv_n(const GemvArgs &a)
 {
     if constexpr (XL == XM_LDS) {
         static const bool lds_raised = [] {
             // a failure here leaves the default limit; the launch then reports it
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL, NM, false>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, true, SPLIT, XL, NM, 0>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
-            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL, NM, false>,
+            (void)hipFuncSetAttribute((const void *)q4_gemv<BF16, R, D, false, SPLIT, XL, NM, 0>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_XLDS_MAX);
             return true;
         }();
         (void)lds_raised;
     }
     const MatrixItems<NM> items = narrow_items<NM>(a.items);
-    // x first in the prefill at one row (x in the ring)
+    // bf16 split-form runs that the prefill holds whole, up to 8 rows: x
+    // first and the corrections ahead of the codes
+    if constexpr (BF16 && SPLIT && R <= 2 && XL != XM_LDS) {
+        if (split_runs_whole(a.plan, a.L, D)) {
+            if (a.plan.nb & 3)
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, 2>), a.grid, a.block, a.lds, a.stream,
+                                   a.x, items, a.M, a.K, a.plan, a.L, a.tps);
+            else
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, 2>), a.grid, a.block, a.lds, a.stream,
+                                   a.x, items, a.M, a.K, a.plan, a.L, a.tps);
+            return;
+        }
+    }
+    // otherwise x first in the prefill at one row (x in the ring)
     if constexpr (R == 1 && XL != XM_LDS) {
         if (a.M == 1) {
             if (a.plan.nb & 3)
-                hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, true>), a.grid, a.block, a.lds, a.stream,
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, 1>), a.grid, a.block, a.lds, a.stream,
                                    a.x, items, a.M, a.K, a.plan, a.L, a.tps);
             else
-                hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, true>), a.grid, a.block, a.lds, a.stream,
+                hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, 1>), a.grid, a.block, a.lds, a.stream,
                                    a.x, items, a.M, a.K, a.plan, a.L, a.tps);
             return;
         }
     }
     if (a.plan.nb & 3)
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, false>), a.grid, a.block, a.lds, a.stream, a.x,
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, true, SPLIT, XL, NM, 0>), a.grid, a.block, a.lds, a.stream, a.x,
                            items, a.M, a.K, a.plan, a.L, a.tps);
     else
-        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, false>), a.grid, a.block, a.lds, a.stream, a.x,
+        hipLaunchKernelGGL((q4_gemv<BF16, R, D, false, SPLIT, XL, NM, 0>), a.grid, a.block, a.lds, a.stream, a.x,
                            items, a.M, a.K, a.plan, a.L, a.tps);
 }
 
