@@ -100,6 +100,24 @@ def test_segment_form_parity_and_bits(M, N, K, bf16):
     assert np.array_equal(y.view(np.uint32), y_mm.view(np.uint32))
 
 
+# bf16 split-form runs that the prefill holds whole (at most 4 quads) take x
+# first and compute every stage's corrections before the codes arrive, up to
+# 8 rows: per-wave x slots (K = 3584, eight runs of 3-4 quads a tile) and
+# DPP-gathered x with runs of 1-2 quads (K = 896), 2-3 quads (K = 1184) and 4
+# quads (K = 992), the last two with a short last quad.
+WHOLE_RUN_SHAPES = [(512, 3584), (300, 896), (70, 1184), (600, 992)]
+
+
+@pytest.mark.parametrize("N,K", WHOLE_RUN_SHAPES)
+def test_runs_held_whole_parity_and_bits(N, K):
+    x, codes, s = synth.problem(N, K, 8, "bf16", workload=94, matrix=N * 7 + K)
+    y_mm = gu.run_linear(x, True, codes, s, kernel="gemm").cpu().numpy().view(np.uint32)
+    for M in range(1, 9):
+        gu.note("whole runs M=%d N=%d K=%d" % (M, N, K))
+        y, _, _ = check(x[:M], True, codes, s, "gemv")
+        assert np.array_equal(y.view(np.uint32), y_mm[:M]), M
+
+
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_one_hot_readout_exact(kernel, bf16):
