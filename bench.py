@@ -300,6 +300,35 @@ def main() -> int:
         launch_floor["us_per_step"] = round(48 * launch_floor["1_workgroups_us"], 1)
         log("empty-kernel launch floor: %s" % launch_floor)
 
+    # ---- reads with the matrix-vector kernels' own streaming structure
+    # (probe_ring_read: each wave streams a contiguous run of 1 KB quads
+    # through a register ring, nothing computed), each launch on another
+    # region of a 1.5 GiB buffer: the floor of a kernel built that way, next
+    # to the per-launch times of the kernels that have that structure.
+    read_structure = None
+    if not (args.headline_only or args.eager_step):
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        plib.q4probe_ring_read.argtypes = [vp, ci, ci, ci, ci, vp, vp]
+        plib.q4probe_ring_read.restype = ci
+        rbytes = 3 << 29
+        rbuf = torch.empty(rbytes, dtype=torch.uint8, device=dev)
+        rsink = torch.zeros(4, dtype=torch.int32, device=dev)
+        read_structure = {}
+        for name, W, Q, wpg, D in (("down_proj split form: 224 workgroups x 8 waves, 19 quads a wave, 4-deep", 1792, 19, 8, 4),
+                                   ("gate_proj segment form: 237 workgroups x 16 waves, 10 quads a wave, 2-deep", 3792, 10, 16, 2),
+                                   ("gate_proj segment form with a 4-deep ring", 3792, 10, 16, 4)):
+            nb = W * Q * 1024
+            calls = rbytes // nb
+            def rr(W=W, Q=Q, wpg=wpg, D=D, nb=nb, calls=calls):
+                st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for i in range(calls):
+                    assert plib.q4probe_ring_read(rbuf.data_ptr() + i * nb, Q, W, wpg, D, rsink.data_ptr(), st) == 0
+            us = best_per_call(rr, calls, tries=3)
+            read_structure[name] = {"bytes": nb, "us": round(us, 2), "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
+        del rbuf
+        torch.cuda.empty_cache()
+        log("read structure floors: %s" % {k: v["us"] for k, v in read_structure.items()})
+
     # ---- inputs, resident in HBM: weights drawn directly in the packed form.
     # Each copy of the set is held as the fused buffers (q|k|v, gate|up,
     # down); the six projections are views into them.
@@ -882,6 +911,7 @@ def main() -> int:
         "detail": {"calibration_read": calib, "parity": parity,
                    "per_m_gbs": per_m, "per_matrix_gbs_m8": per_matrix_m8, "per_launch_us": per_launch_us,
                    "grouped_step": grouped_step, "fused_step": fused_step, "mixed_124": mixed, "issue_overlap": issue, "launch_floor": launch_floor,
+                   "read_structure": read_structure,
                    "decode_stream_7b": stream, "small_workloads": small or None, "switching_schemes": schemes,
                    "crossover": crossover, "records": records.rows},
     }

@@ -15,6 +15,12 @@
 // yardstick of the bandwidth the memory system delivers to a simple kernel
 // ("a big copy, not the spec sheet", in "Why LLM Decoding Is Slow, and Why
 // Batching Is (Almost) Free", section "First Attempt: A Faster Chip").
+//
+// probe_ring_read reads with the matrix-vector kernels' streaming structure
+// and nothing else: each wave streams its own contiguous run of 1 KB quads
+// (16 bytes a lane, non-temporal) through a D-deep register ring, in
+// workgroups of a given number of waves; the benchmark's floor for a kernel
+// of that structure.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,6 +100,39 @@ __global__ __launch_bounds__(512) void probe_read(const q4::u32x4 *__restrict__ 
     const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
     if (r == 0x9E3779B9u)
         sink[0] = r;
+}
+
+// Wave w (of W) streams quads w Q .. w Q + Q - 1 (1 KB each, lane l reading
+// bytes 16 l .. 16 l + 15) with D loads in flight; refills past the run read
+// its last quad again (in range).  The xor of everything read goes to
+// sink[0] only if it equals a value no real buffer is known to give.
+template <int D>
+__global__ __launch_bounds__(1024) void probe_ring_read(const q4::u32x4 *__restrict__ src, int Q, int W,
+                                                        uint32_t *sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (w >= W)
+        return;
+    const q4::u32x4 *run = src + (size_t)w * Q * 64 + lane;
+    q4::u32x4 r[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        r[u] = __builtin_nontemporal_load(run + 64 * (size_t)min(u, Q - 1));
+    q4::u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int q = 0; q < Q; q += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            acc ^= r[u];
+            r[u] = __builtin_nontemporal_load(run + 64 * (size_t)min(q + u + D, Q - 1));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        acc ^= r[u];
+    const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (v == 0x9E3779B9u)
+        sink[0] = v;
 }
 
 // Issue-overlap probe: per iteration a wave runs 4 independent bf16 block
@@ -184,6 +223,25 @@ int q4probe_read(const void *src, size_t bytes, void *sink, int blocks, void *st
         return -1;
     hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(512), 0, (hipStream_t)stream, (const q4::u32x4 *)src,
                        bytes / 16, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Reads waves x quads KB from src (16-byte aligned) with the streaming
+// structure of probe_ring_read: workgroups of waves_per_group (1..16) waves,
+// depth 2 or 4.
+int q4probe_ring_read(const void *src, int quads, int waves, int waves_per_group, int depth, void *sink,
+                      void *stream)
+{
+    if (!src || !sink || quads < 1 || waves < 1 || waves_per_group < 1 || waves_per_group > 16 ||
+        (depth != 2 && depth != 4))
+        return -1;
+    const dim3 grid((unsigned)((waves + waves_per_group - 1) / waves_per_group)), block(64u * waves_per_group);
+    if (depth == 2)
+        hipLaunchKernelGGL(probe_ring_read<2>, grid, block, 0, (hipStream_t)stream, (const q4::u32x4 *)src, quads,
+                           waves, (uint32_t *)sink);
+    else
+        hipLaunchKernelGGL(probe_ring_read<4>, grid, block, 0, (hipStream_t)stream, (const q4::u32x4 *)src, quads,
+                           waves, (uint32_t *)sink);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
