@@ -1715,6 +1715,12 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
     if (sh.split && M <= 8)
         sh.xm = plan.S / sh.L == 8 || (tiles > 256 && (M <= 4 || plan.G >= 8)) ? XM_WAVE : XM_QUAD;
+    // One row with eight runs a tile and K >= 8192: x staged once per
+    // workgroup instead of per-wave slots, so the loop issues no x loads
+    // (down_proj 10.2 -> 9.8 us, 3584 x 14336 8.25 -> 7.95 us; at 2 and 4
+    // rows slower on down_proj, 9.9 -> 10.4 and 10.4 -> 11.4 us)
+    if (sh.split && M == 1 && plan.S / sh.L == 8 && plan.G >= 64 && fits)
+        sh.xm = XM_LDS;
     sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
     if (sh.xm != XM_LDS && sh.split)
         sh.D = 4;  // x rides in the ring: up to 22 registers a stage

@@ -63,8 +63,9 @@ SHAPES = [
     (3, 4100, 3584, True), (2, 4100, 4128, True), (7, 6150, 4864, False),
     (3, 65552, 1024, True), (6, 65552, 1024, False),
     # one row: the prefill's x first (per-wave slots; a run the prefill
-    # holds whole, and a long one)
-    (1, 512, 3584, True), (1, 130, 18944, True),
+    # holds whole, and a longer one), and x staged once per workgroup for
+    # K >= 8192 with eight runs a tile (bf16; fp16 with a short last quad)
+    (1, 512, 3584, True), (1, 200, 4864, True), (1, 130, 18944, True), (1, 70, 8224, False),
 ]
 
 
