@@ -828,11 +828,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
 //    A operands through its own LDS slot (gate at 5 rows 10.3 -> 9.8 us,
 //    gate|up 17.4 -> 16.7 us); otherwise each wave loads them directly,
 //    four 16-byte loads a quad;
-//  * with whole ring rounds of four stages (LQ <= 2, R <= 2) the scales come
-//    in groups of four positions, one 8-byte load a lane for the group: the
-//    lanes of row g load position g's column scales and each position's reach
-//    every row by ds_bpermute (gate 10.1 -> 9.9 us, gate|up 17.6 -> 16.8 us,
-//    both together 10.1 -> 9.4 us at one to four rows).
+//  * with rings of four or two stages (LQ <= 2, R <= 2) the scales come in
+//    groups of one ring round's positions, one 8-byte load a lane for the
+//    group: the lanes of row g load position g's column scales and each
+//    position's reach every row by ds_bpermute (four stages: gate 10.1 ->
+//    9.9 us, gate|up 17.6 -> 16.8 us, both together 10.1 -> 9.4 us at one
+//    to four rows; two stages: gate 8.92 -> 8.77 us at one row).
 // grid = (sum over the matrices of ceil(tiles / tpw), ceil(M / 16)),
 // block = 1024; a workgroup's matrix is the one whose range of workgroup
 // ids holds it (see MatrixItems).  With MR =
