@@ -13,9 +13,9 @@
 //    issued D quads ahead without branches), dequantizes in registers while
 //    reading (the matrix-vector kernel's advantage the page names) and runs
 //    the block dots on MFMA with all (<= 16) rows of x in the A operand
-//    (x staged in LDS, passed through per-wave LDS slots, gathered by DPP or
-//    loaded with the ring: see XM_RING).  The runs' subtree roots meet in
-//    LDS for the top of the pairwise tree.
+//    (x staged in LDS, loaded in the slot layout that gives one MFMA the
+//    corrections of a whole quad, or loaded with the ring: see XM_RING).
+//    The runs' subtree roots meet in LDS for the top of the pairwise tree.
 //
 //  * q4_gemv_seg: the same kernel's form for wide N (more than 256 or 512
 //    column tiles, see seg_shape): a workgroup of 16 waves owns a run of
@@ -150,6 +150,88 @@ __device__ __forceinline__ void gemv_quad_pre(const GemvStage &st, const u32x4 (
     }
 }
 
+// One batch row per lane group (R = 1) with x in the slot layout: A row slot
+// 4 i + j holds batch row i's block j of the quad (lane (g, 4 i + j) holds
+// that block's k-slots 8 g .. 8 g + 7; the loads of XM_SLOT, or one read of
+// x staged in LDS).  One correction MFMA then gives every (row, block) pair
+// its correction in its own slot, and block j's dot runs on the same A
+// operand with that accumulator input: row i's value lands in slot 4 i + j,
+// component j of lane group i.  An MFMA result element depends only on its
+// own A row, B column and accumulator input, so these are the bits of the
+// one-block-per-dot form (same instruction, same operands), with 5 MFMAs a
+// quad instead of 8 and no gathering of x.
+template <bool BF16, bool SHORT>
+__device__ __forceinline__ void gemv_quad_slots(const u32x4 &w, const u32x2 &s, const u32x4 &a, int nq,
+                                                const Dequant<BF16> &dq, float (&p)[1])
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t h[4] = {s.x & 0xFFFFu, s.x >> 16, s.y & 0xFFFFu, s.y >> 16};
+    const f32x4 C = correction<BF16>(a, dq);
+    f32x4 D[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        D[i] = block_dot<BF16>(a, dq(wd[i]), C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (!SHORT || i < nq)
+            p[0] = __builtin_fmaf(half_bits_to_float(h[i]), D[i][i], p[0]);
+}
+
+// The block values of a quad in the slot layout (bv[i][0]: block i).
+template <bool BF16>
+__device__ __forceinline__ void gemv_block_values_slots(const u32x4 &w, const u32x4 &a, const Dequant<BF16> &dq,
+                                                        float (&bv)[4][1])
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const f32x4 C = correction<BF16>(a, dq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        bv[i][0] = block_dot<BF16>(a, dq(wd[i]), C)[i];
+}
+
+// Two batch rows per lane group (R = 2) in the slot layout of XM_SLOT's
+// loads: operand a holds blocks 0 and 1 of the quad, operand b blocks 2 and
+// 3, A row slot 4 i + k holding row i + 4 (k & 1) of block k >> 1 (of the
+// pair).  One correction MFMA per operand covers its four (row, block)
+// pairs; the first block of a pair lands in components 0 (row i) and 1 (row
+// i + 4) of lane group i, the second in components 2 and 3.  6 MFMAs a quad
+// instead of 8, the same bits (as in gemv_quad_slots).
+template <bool BF16, bool SHORT>
+__device__ __forceinline__ void gemv_quad_slots2(const u32x4 &w, const u32x2 &s, const u32x4 &a, const u32x4 &b,
+                                                 int nq, const Dequant<BF16> &dq, float (&p)[2])
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t h[4] = {s.x & 0xFFFFu, s.x >> 16, s.y & 0xFFFFu, s.y >> 16};
+    const f32x4 Ca = correction<BF16>(a, dq), Cb = correction<BF16>(b, dq);
+    f32x4 D[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        D[i] = block_dot<BF16>(i < 2 ? a : b, dq(wd[i]), i < 2 ? Ca : Cb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!SHORT || i < nq) {
+            const float d = half_bits_to_float(h[i]);
+            p[0] = __builtin_fmaf(d, D[i][2 * (i & 1)], p[0]);
+            p[1] = __builtin_fmaf(d, D[i][2 * (i & 1) + 1], p[1]);
+        }
+    }
+}
+
+// The block values of a quad in the two-row slot layout (bv[i][r]).
+template <bool BF16>
+__device__ __forceinline__ void gemv_block_values_slots2(const u32x4 &w, const u32x4 &a, const u32x4 &b,
+                                                         const Dequant<BF16> &dq, float (&bv)[4][2])
+{
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const f32x4 Ca = correction<BF16>(a, dq), Cb = correction<BF16>(b, dq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = block_dot<BF16>(i < 2 ? a : b, dq(wd[i]), i < 2 ? Ca : Cb);
+        bv[i][0] = v[2 * (i & 1)];
+        bv[i][1] = v[2 * (i & 1) + 1];
+    }
+}
+
 // The wave's stream is a contiguous run of tile-quads: quad i of the stream
 // sits at code byte 1024 i and scale byte 128 i from the wave's base, and is
 // quad q0 + (i mod RQ) of K.  The code and scale resources span exactly the
@@ -160,29 +242,24 @@ __device__ __forceinline__ void gemv_quad_pre(const GemvStage &st, const u32x4 (
 struct GemvStream {
     __amdgpu_buffer_rsrc_t w, s, x;
     uint32_t w_lane, s_lane, x_lane;  // per-lane byte offsets
-    uint32_t xw_lane[2];              // XM_WAVE: rows g, 4 + g, chunk c; XM_QUAD: see gemv_x_quad
+    uint32_t xw_lane[2];              // XM_SLOT: the (row, block) pairs of the lane's slots
     uint32_t w_off, s_off;            // scalar offsets of the next refill
 };
 
 // Where the matrix-vector kernel's A operands (x) come from.
 //  XM_RING: loaded with each ring stage in the A-operand layout: four
 //    16-byte loads a lane (one per block), whatever the row count.
-//  XM_LDS: the workgroup's rows copied into LDS once, before the loop.
-//  XM_WAVE: loaded with each ring stage in row order, 256 contiguous bytes a
-//    row (one 16-byte load a lane per four rows: R loads), and turned into
-//    the A-operand layout through a per-wave LDS slot.  The cache lines x's
-//    loads request per stage bound these streams: at eight rows XM_RING
-//    requests 32 a stage (each load touches 64 bytes of 8 rows) and XM_WAVE
-//    16 (each line once); measured on MI355X, down_proj at eight rows takes
-//    16.0 us and 13.3 us.
-//  XM_QUAD: up to 8 rows, loaded with each ring stage into the A-operand
-//    layout by the lanes of the unused row slots as well, so that each load
-//    reads whole 128-byte lines of its rows, then moved within each quad of
-//    lanes by DPP (no LDS).
-enum : int { XM_RING = 0, XM_LDS = 1, XM_WAVE = 2, XM_QUAD = 3 };
-// Bytes of a row in an XM_WAVE slot: 256 and 16 of padding, so that rows
-// start in different banks.
-constexpr uint32_t XW_ROW = 272;
+//  XM_LDS: the workgroup's rows copied into LDS once, before the loop (the
+//    split form reads them in the slot layout).
+//  XM_SLOT: up to 8 rows, loaded with each ring stage in the slot layout
+//    (gemv_quad_slots, gemv_quad_slots2): the lanes of the row slots that
+//    hold no batch row load other blocks of the rows, so that each load
+//    reads whole 128-byte lines and the A operands need no gathering.
+//    Measured on MI355X against rows loaded in row order and turned into the
+//    A-operand layout through a per-wave LDS slot: q_proj at 1 / 8 rows 4.34
+//    / 4.90 -> 4.11 / 4.74 us, down_proj at 2 rows 10.22 -> 9.34 us; and
+//    that slot form against XM_RING at 8 rows, down_proj 16.0 -> 13.3 us.
+enum : int { XM_RING = 0, XM_LDS = 1, XM_SLOT = 3 };
 
 // Keeps the ring's loads in program order relative to their uses: the empty
 // statement (no instructions) with a memory clobber stops IR-level motion,
@@ -196,7 +273,7 @@ __device__ __forceinline__ void issue_fence()
 // Loads one stage: the next quad of the stream and, unless x is staged in
 // LDS (XM_LDS), the x of quad x_off / 256 (x_off >= the slice size for a
 // refill past the stream's end): the four A-operand blocks (XM_RING) or NW
-// loads of four rows each (XM_WAVE, into xa[0 .. NW - 1]).
+// slot-layout operands (XM_SLOT, into xa[0 .. NW - 1]).
 template <int XM, int NW>
 __device__ __forceinline__ void gemv_load_x(GemvStage &st, GemvStream &in, uint32_t x_off)
 {
@@ -205,7 +282,7 @@ __device__ __forceinline__ void gemv_load_x(GemvStage &st, GemvStream &in, uint3
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b + x_off, 0, 0));
-    } else if constexpr (XM == XM_WAVE || XM == XM_QUAD) {
+    } else if constexpr (XM == XM_SLOT) {
 #pragma unroll
         for (int j = 0; j < NW; ++j)
             st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j] + x_off, 0, 0));
@@ -226,8 +303,8 @@ __device__ __forceinline__ void gemv_load(GemvStage &st, GemvStream &in, uint32_
         for (int b = 0; b < 4; ++b)
             st.xa[b] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.x_lane + 64u * b + x_off, 0, 0));
-    } else if constexpr (XM == XM_WAVE || XM == XM_QUAD) {
-        static_assert(NW == 1 || NW == 2, "XM_WAVE and XM_QUAD hold up to 8 rows");
+    } else if constexpr (XM == XM_SLOT) {
+        static_assert(NW == 1 || NW == 2, "XM_SLOT holds up to 8 rows");
 #pragma unroll
         for (int j = 0; j < NW; ++j)
             st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(in.x, in.xw_lane[j] + x_off, 0, 0));
@@ -243,59 +320,6 @@ __device__ __forceinline__ void gemv_x_lds(u32x4 (&xa)[4], const uint8_t *xrow, 
 #pragma unroll
     for (int b = 0; b < 4; ++b)
         xa[b] = *(const u32x4 *)(xrow + 256 * q + 64 * b);
-}
-
-// DPP quad permutation of a 16-byte fragment: lane i of each quad of lanes
-// takes the fragment of lane (CTRL >> 2 i) & 3.
-template <int CTRL>
-__device__ __forceinline__ u32x4 quad_perm(const u32x4 &v)
-{
-    return u32x4{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, CTRL, 0xF, 0xF, false),
-                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, CTRL, 0xF, 0xF, false),
-                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, CTRL, 0xF, 0xF, false),
-                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, CTRL, 0xF, 0xF, false)};
-}
-
-// XM_QUAD: the A operands of a stage.  Live rows sit in row slots c with
-// c mod 4 in {0, 1} (R = 2) or c mod 4 == 0 (R = 1):
-//   R = 1: lane 4i + j loaded block j of the row of slot 4i; lane 4i
-//          gathers blocks 1..3 from lanes 4i + 1 .. 4i + 3;
-//   R = 2: lane 4i + h (h = 0, 1) loaded blocks 0 and 2 of its row, lane
-//          4i + 2 + h blocks 1 and 3 of the same row; the live lanes take
-//          those.
-// Lanes of unused slots end with fragments of other rows: those rows'
-// outputs are never stored.
-template <int R>
-__device__ __forceinline__ void gemv_x_quad(u32x4 (&xa)[4], const GemvStage &st)
-{
-    if constexpr (R == 1) {
-        xa[0] = st.xa[0];
-        xa[1] = quad_perm<0x55>(st.xa[0]);
-        xa[2] = quad_perm<0xAA>(st.xa[0]);
-        xa[3] = quad_perm<0xFF>(st.xa[0]);
-    } else {
-        xa[0] = st.xa[0];
-        xa[1] = quad_perm<0xEE>(st.xa[0]);
-        xa[2] = st.xa[1];
-        xa[3] = quad_perm<0xEE>(st.xa[1]);
-    }
-}
-
-// XM_WAVE: the stage's rows (lane (g, c) of load j holds chunk c of row
-// 4 j + g) through the wave's LDS slot into the A-operand layout (lane (g, c)
-// reads row slot c's k-slots 8g..8g+7 of each block).  wput: the lane's
-// chunk of load 0 in the slot; xget: its A row in the slot, 16 g added.
-// LDS operations of one wave complete in order, so the reads see the writes
-// and the next stage's writes cannot overtake them.
-template <int NW>
-__device__ __forceinline__ void gemv_x_wave(u32x4 (&xa)[4], const GemvStage &st, uint8_t *wput, const uint8_t *xget)
-{
-#pragma unroll
-    for (int j = 0; j < NW; ++j)
-        *(u32x4 *)(wput + 4 * XW_ROW * j) = st.xa[j];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        xa[b] = *(const u32x4 *)(xget + 64 * b);
 }
 
 // Row slots of a 16-row slice.  Batch row m sits in A-operand row slot
@@ -367,14 +391,14 @@ __device__ __forceinline__ MatrixSel select_matrix(const MatrixItems<NM> items)
 //    column tiles, wave (slot, run) streams run `run` (segments run L ..
 //    run L + L - 1) of tile slot `slot`; each tile's W run roots meet in LDS
 //    for the top of the pairwise tree.
-//  XM (see XM_RING, XM_LDS, XM_WAVE): where the A operands come from.
+//  XM (see XM_RING, XM_LDS, XM_SLOT): where the A operands come from.
 //  XF: 0, x loaded with each stage's codes; 1 (one row), x first in the
 //    prefill; 2 (bf16 split form, up to 8 rows, every run held whole by the
 //    prefill), x first and the corrections of all stages computed while the
 //    codes are still in flight.
 // Dynamic LDS: [4 waves][tps tiles][16][16] tile roots (SPLIT = false), then
 // (XM_LDS) min(M, 16) rows of gemv_xrow_bytes(K) bytes and 256 bytes of
-// slack, or (XM_WAVE) one slot of 4 R rows of XW_ROW bytes per wave.
+// slack.
 template <bool BF16, int R, int D, bool SHORT, bool SPLIT, int XM, int NM, int XF>
 __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__restrict__ x, MatrixItems<NM> items,
                                                               int M, int K, Plan plan, int L, int tps)
@@ -447,8 +471,10 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     // rows that are never stored
     const int xr = slot_row(c);  // the batch row of A row slot c
     in.x_lane = xr < mrows ? (uint32_t)xr * (uint32_t)K * 2u + 16u * g : x_bytes;
-    if constexpr (XM == XM_QUAD) {
-        // the quad partner's row and the blocks this lane loads for it
+    if constexpr (XM == XM_SLOT) {
+        // the slot layout: lane (g, 4 i + k) loads, for operand j, batch row
+        // i (R = 1) or i + 4 (k & 1) (R = 2) and block k (R = 1) or 2 j +
+        // (k >> 1) (R = 2), k-slots 8 g .. 8 g + 7
         const int pc = R == 1 ? (c & ~3) : (c & ~2);
         const int qr = slot_row(pc);
 #pragma unroll
@@ -456,16 +482,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             const int b = R == 1 ? (c & 3) : 2 * j + ((c >> 1) & 1);
             in.xw_lane[j] = qr < mrows ? (uint32_t)qr * (uint32_t)K * 2u + 64u * (uint32_t)b + 16u * g : x_bytes;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            in.xw_lane[j] = 4 * j + g < mrows ? (uint32_t)(4 * j + g) * (uint32_t)K * 2u + 16u * c : x_bytes;
     }
-    // XM_WAVE: the wave's slot; A rows past the batch read the last row
-    // (their outputs are never stored)
-    uint8_t *const wslot = xlds + (uint32_t)wave * (4u * R * XW_ROW);
-    uint8_t *const wput = wslot + (uint32_t)g * XW_ROW + 16u * c;
-    const uint8_t *const xget = wslot + (uint32_t)min(xr, mrows - 1) * XW_ROW + 16u * g;
     in.w_off = 0;
     in.s_off = 0;
 
@@ -544,6 +561,14 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         issue_fence();
     }
     const uint8_t *xrow = xlds + (uint32_t)min(xr, mrows - 1) * gemv_xrow_bytes(K) + 16 * g;
+    // x in the slot layout (gemv_quad_slots, gemv_quad_slots2): the loads of
+    // XM_SLOT as they are, or (one row per lane group) one read of the staged
+    // rows (rows past the batch read the last row: their slots are never
+    // stored)
+    constexpr bool SLOTS = R == 1 && (XM == XM_SLOT || XM == XM_LDS);
+    constexpr bool SLOTS2 = R == 2 && XM == XM_SLOT;
+    const uint8_t *xslot =
+        xlds + (uint32_t)min(c >> 2, mrows - 1) * gemv_xrow_bytes(K) + 64u * (uint32_t)(c & 3) + 16u * (uint32_t)g;
     if constexpr (XL) {
         x_round_store(0);
         for (int i0 = 8 * (int)blockDim.x; i0 < nch; i0 += 8 * (int)blockDim.x) {
@@ -576,8 +601,12 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
     int li = 0;   // segment within the run
     int seg_end = ((seg0 + 1) * G) >> plan.log2S;
     u32x4 xb[2][4];  // XL: x of the quad being computed and of the next
-    if constexpr (XL)
-        gemv_x_lds(xb[0], xrow, q0);
+    if constexpr (XL) {
+        if constexpr (SLOTS)
+            xb[0][0] = *(const u32x4 *)(xslot + 256u * (uint32_t)q0);
+        else
+            gemv_x_lds(xb[0], xrow, q0);
+    }
     // after quad qc's scale-accumulates: at a segment's end, fold it into the
     // run's subtree
     auto finish_quad = [&](int qn) {
@@ -632,19 +661,55 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
         // codes are there (guarded: only the stages the run holds)
         auto ahead = [&](auto guarded) {
             constexpr bool GD = decltype(guarded)::value;
+            if constexpr (SLOTS) {  // one correction a stage
+                f32x4 C1[D];
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (!GD || d < total)
+                        C1[d] = correction<BF16>(ring[d].xa[0], dq);
+                issue_fence();
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    if (!GD || d < total) {
+                        const uint32_t w[4] = {ring[d].w.x, ring[d].w.y, ring[d].w.z, ring[d].w.w};
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            bv[d][b][0] = block_dot<BF16>(ring[d].xa[0], dq(w[b]), C1[d])[b];
+                    }
+                }
+                return;
+            }
+            if constexpr (SLOTS2) {  // two corrections a stage
+                f32x4 C2[D][2];
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (!GD || d < total) {
+                        C2[d][0] = correction<BF16>(ring[d].xa[0], dq);
+                        C2[d][1] = correction<BF16>(ring[d].xa[1], dq);
+                    }
+                issue_fence();
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    if (!GD || d < total) {
+                        const uint32_t w[4] = {ring[d].w.x, ring[d].w.y, ring[d].w.z, ring[d].w.w};
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const f32x4 v = block_dot<BF16>(ring[d].xa[b >> 1], dq(w[b]), C2[d][b >> 1]);
+                            bv[d][b][0] = v[2 * (b & 1)];
+                            bv[d][b][1] = v[2 * (b & 1) + 1];
+                        }
+                    }
+                }
+                return;
+            }
             u32x4 xa[D][4];
             f32x4 C[D][4];
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 if (!GD || d < total) {
-                    if constexpr (XM == XM_WAVE)
-                        gemv_x_wave<R>(xa[d], ring[d], wput, xget);
-                    else if constexpr (XM == XM_QUAD)
-                        gemv_x_quad<R>(xa[d], ring[d]);
-                    else
 #pragma unroll
-                        for (int b = 0; b < 4; ++b)
-                            xa[d][b] = ring[d].xa[b];
+                    for (int b = 0; b < 4; ++b)
+                        xa[d][b] = ring[d].xa[b];
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
                         C[d][b] = correction<BF16>(xa[d][b], dq);
@@ -666,16 +731,15 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             }
         };
         auto stage_values = [&](int d) {
-            u32x4 xa[4];
-            if constexpr (XM == XM_WAVE)
-                gemv_x_wave<R>(xa, ring[d], wput, xget);
-            else if constexpr (XM == XM_QUAD)
-                gemv_x_quad<R>(xa, ring[d]);
-            else
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    xa[b] = ring[d].xa[b];
-            gemv_block_values<BF16, R>(ring[d], xa, dq, bv[d]);
+            if constexpr (SLOTS) {
+                gemv_block_values_slots<BF16>(ring[d].w, ring[d].xa[0], dq, bv[d]);
+                return;
+            }
+            if constexpr (SLOTS2) {
+                gemv_block_values_slots2<BF16>(ring[d].w, ring[d].xa[0], ring[d].xa[1], dq, bv[d]);
+                return;
+            }
+            gemv_block_values<BF16, R>(ring[d], ring[d].xa, dq, bv[d]);
         };
         // (a run one stage short of the ring computes the spare stage on
         // zeros rather than branch around it: no branch splits the stages'
@@ -732,16 +796,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256) void q4_gemv(const uint16_t *__r
             const int ii = base + d;
             if (ii < total) {
                 const int qn = qc + 1 == q1 ? q0 : qc + 1;
-                if constexpr (XL)
-                    gemv_x_lds(xb[(d + 1) & 1], xrow, qn);
-                if constexpr (XM == XM_WAVE) {
-                    u32x4 xa[4];
-                    gemv_x_wave<R>(xa, ring[d], wput, xget);
-                    gemv_quad<BF16, R, SHORT>(ring[d], xa, SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
-                } else if constexpr (XM == XM_QUAD) {
-                    u32x4 xa[4];
-                    gemv_x_quad<R>(xa, ring[d]);
-                    gemv_quad<BF16, R, SHORT>(ring[d], xa, SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                if constexpr (XL) {
+                    if constexpr (SLOTS)
+                        xb[(d + 1) & 1][0] = *(const u32x4 *)(xslot + 256u * (uint32_t)qn);
+                    else
+                        gemv_x_lds(xb[(d + 1) & 1], xrow, qn);
+                }
+                if constexpr (SLOTS) {
+                    gemv_quad_slots<BF16, SHORT>(ring[d].w, ring[d].s, XL ? xb[d & 1][0] : ring[d].xa[0],
+                                                 SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
+                } else if constexpr (SLOTS2) {
+                    gemv_quad_slots2<BF16, SHORT>(ring[d].w, ring[d].s, ring[d].xa[0], ring[d].xa[1],
+                                                  SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
                 } else {
                     gemv_quad<BF16, R, SHORT>(ring[d], XL ? xb[d & 1] : ring[d].xa,
                                               SHORT ? min(4, plan.nb - 4 * qc) : 4, dq, p);
@@ -1650,7 +1716,7 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint8_t *__restrict_
 
 struct GemvShape {
     bool split;
-    int xm;  // XM_RING, XM_LDS or XM_WAVE
+    int xm;  // XM_RING, XM_LDS or XM_SLOT
     int L, tps, D, tw;  // tw: column tiles per split workgroup
     size_t lds;  // dynamic LDS bytes
 };
@@ -1707,30 +1773,24 @@ static GemvShape gemv_shape(int M, int N, const Plan &plan, int K)
     const size_t roots = sh.split ? 0 : (size_t)4 * sh.tps * 256 * sizeof(float);
     const bool fits = roots + xbytes <= GEMV_XLDS_MAX;
     // Measured on MI355X, weights streaming from HBM.  Split form up to 8
-    // rows: with eight runs a tile (K = 4096, 4864, 8192, 18944) x through
-    // per-wave slots (down_proj at 4 / 8 rows 11.9 / 15.8 -> 10.6 / 13.3 us
-    // against the staged / ring forms), and so for more than 256 tiles up to
-    // 4 rows or from K = 1024 (against DPP gathering: 4608 x 3584 at 4 rows
-    // 6.24 -> 5.98 us, 6144 x 4864 7.6 -> 7.2 us, 4864 x 896 4.13 -> 3.99
-    // us; not 8192 x 512 at 5-8 rows), otherwise x gathered by DPP (at 1-4
-    // rows against staging: 4864 x 896 4.3 -> 3.8 us, 2048 x 2048 3.9 ->
-    // 3.6 us; at 5-8 rows against the ring: k_proj 4.75 -> 4.67 us).  One
+    // rows: x loaded in the slot layout and used as loaded
+    // (gemv_quad_slots / gemv_quad_slots2: 5 or 6 MFMAs a quad, no gathering
+    // of x), except at one row with eight runs a tile and K >= 8192, where x
+    // is staged once per workgroup and read in the same layout, so the loop
+    // issues no x loads.  Against x through per-wave LDS slots: q_proj at 1 /
+    // 4 / 5 / 8 rows 4.34 / 4.40 / 4.72 / 4.90 -> 4.11 / 4.23 / 4.45 / 4.74
+    // us, k_proj 3.77 / 3.98 / 4.25 / 4.47 -> 3.57 / 3.80 / 4.04 / 4.36 us,
+    // down_proj at 2 / 4 / 5 rows 10.22 / 10.58 / 11.6 -> 9.34 / 10.21 /
+    // 11.2 us (8 rows: 12.6 either way); staged at one row: down_proj 9.70
+    // -> 9.30 us (at 2 and 4 rows staging costs more than it saves).  One
     // stream per wave (very wide N): x staged up to 4 rows, else in the ring.
     sh.xm = fits && M <= 4 ? XM_LDS : XM_RING;
     if (sh.split && M <= 8)
-        sh.xm = plan.S / sh.L == 8 || (tiles > 256 && (M <= 4 || plan.G >= 8)) ? XM_WAVE : XM_QUAD;
-    // One row with eight runs a tile and K >= 8192: x staged once per
-    // workgroup instead of per-wave slots, so the loop issues no x loads
-    // (down_proj 10.2 -> 9.8 us, 3584 x 14336 8.25 -> 7.95 us; at 2 and 4
-    // rows slower on down_proj, 9.9 -> 10.4 and 10.4 -> 11.4 us)
-    if (sh.split && M == 1 && plan.S / sh.L == 8 && plan.G >= 64 && fits)
-        sh.xm = XM_LDS;
+        sh.xm = M == 1 && plan.S / sh.L == 8 && plan.G >= 64 && fits ? XM_LDS : XM_SLOT;
     sh.tw = 1;  // larger workgroups sharing one copy of x measured slower
     if (sh.xm != XM_LDS && sh.split)
         sh.D = 4;  // x rides in the ring: up to 22 registers a stage
-    const int waves = sh.split ? (plan.S / sh.L) * sh.tw : 4;
-    const size_t wslots = (size_t)waves * 4 * (rows <= 4 ? 1 : 2) * XW_ROW;
-    sh.lds = roots + (sh.xm == XM_LDS ? xbytes : sh.xm == XM_WAVE ? wslots : 0);
+    sh.lds = roots + (sh.xm == XM_LDS ? xbytes : 0);
     return sh;
 }
 
@@ -1850,9 +1910,9 @@ static void launch_gemv_v(const GemvArgs &a)
     launch_gemv_n<BF16, R, D, SPLIT, XL, 1>(a);
 }
 
-// Built variants: x in LDS with a 4-deep ring; x through per-wave slots
-// (up to 8 rows) with a 4-deep ring; x in the ring with a 4-deep (split) or
-// 4/8-deep (one stream per wave) ring.
+// Built variants: x in LDS with a 4-deep ring; x in the slot layout (split
+// form, up to 8 rows) with a 4-deep ring; x in the ring with a 4-deep
+// (split) or 4/8-deep (one stream per wave) ring.
 template <bool BF16, int R>
 static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
 {
@@ -1865,19 +1925,8 @@ static void launch_gemv_r(const GemvShape &sh, const GemvArgs &a)
         return;
     }
     if constexpr (R <= 2) {
-        if (sh.xm == XM_QUAD) {
-            if (sh.split)
-                launch_gemv_v<BF16, R, 4, true, XM_QUAD>(a);
-            else
-                launch_gemv_v<BF16, R, 4, false, XM_QUAD>(a);
-            return;
-        }
-        if (sh.xm == XM_WAVE) {
-            constexpr int DW = 4;
-            if (sh.split)
-                launch_gemv_v<BF16, R, DW, true, XM_WAVE>(a);
-            else
-                launch_gemv_v<BF16, R, DW, false, XM_WAVE>(a);
+        if (sh.xm == XM_SLOT) {  // (split form only)
+            launch_gemv_v<BF16, R, 4, true, XM_SLOT>(a);
             return;
         }
     }

@@ -48,8 +48,9 @@ def test_hand_example_exact(kernel):
 # (M, N, K, bf16): several tiles, ragged N and M tails, K with a short last
 # quad, the smallest K, segment counts 1..16; K above 8192 with a short last
 # quad (the matrix-matrix kernel's 32-row units, split over K); eight runs a
-# tile with a short last quad at 2..8 rows (x through per-wave LDS slots);
-# 5..8 rows with fewer runs, one with a short last quad (x gathered by DPP);
+# tile with a short last quad at 2..8 rows and 5..8 rows with fewer runs,
+# one with a short last quad (x in the slot layout, one and two rows per lane
+# group);
 # 4097 column tiles with K outside the segment form's range (one stream per
 # wave: x staged in LDS up to 4 rows, else in the ring)
 SHAPES = [
@@ -62,9 +63,10 @@ SHAPES = [
     (6, 300, 3616, True), (8, 40, 896, False),
     (3, 4100, 3584, True), (2, 4100, 4128, True), (7, 6150, 4864, False),
     (3, 65552, 1024, True), (6, 65552, 1024, False),
-    # one row: the prefill's x first (per-wave slots; a run the prefill
-    # holds whole, and a longer one), and x staged once per workgroup for
-    # K >= 8192 with eight runs a tile (bf16; fp16 with a short last quad)
+    # one row: the prefill's x first (slot layout; a run the prefill holds
+    # whole, and a longer one), and x staged once per workgroup for K >= 8192
+    # with eight runs a tile, read in the slot layout (bf16; fp16 with a
+    # short last quad)
     (1, 512, 3584, True), (1, 200, 4864, True), (1, 130, 18944, True), (1, 70, 8224, False),
 ]
 
@@ -103,9 +105,9 @@ def test_segment_form_parity_and_bits(M, N, K, bf16):
 
 # bf16 split-form runs that the prefill holds whole (at most 4 quads) take x
 # first and compute every stage's corrections before the codes arrive, up to
-# 8 rows: per-wave x slots (K = 3584, eight runs of 3-4 quads a tile) and
-# DPP-gathered x with runs of 1-2 quads (K = 896), 2-3 quads (K = 1184) and 4
-# quads (K = 992), the last two with a short last quad.
+# 8 rows, x in the slot layout: eight runs of 3-4 quads a tile (K = 3584) and
+# runs of 1-2 quads (K = 896), 2-3 quads (K = 1184) and 4 quads (K = 992),
+# the last two with a short last quad.
 WHOLE_RUN_SHAPES = [(512, 3584), (300, 896), (70, 1184), (600, 992)]
 
 
